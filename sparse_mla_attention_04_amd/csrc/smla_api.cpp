@@ -1,0 +1,297 @@
+// C ABI of the sparse MLA library: validation, planning, workspace sizing and
+// launch.  Validation runs entirely on the host before any HIP call, so every
+// argument error returns without touching the device.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "../../include/sparse_mla.h"
+#include "smla_internal.h"
+
+namespace {
+
+constexpr int64_t kPartialFloatsPerHead = SMLA_D_V + 1;   // normalised out + lse
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int log2i(int64_t v) {
+  int s = 0;
+  while ((int64_t(1) << s) < v) ++s;
+  return s;
+}
+
+// Parameter checks that need no pointers.
+int check_params(const smla_params* p) {
+  if (!p) return SMLA_ERR_INVALID_ARG;
+  if (p->kernel_variant < 0) return SMLA_ERR_INVALID_ARG;
+  if (p->num_tokens < 0) return SMLA_ERR_INVALID_ARG;
+  if (p->num_heads < 1) return SMLA_ERR_INVALID_ARG;
+  if (p->num_heads > SMLA_MAX_HEADS) return SMLA_ERR_UNSUPPORTED;
+  if (p->topk < 1 || p->idx_stride < p->topk) return SMLA_ERR_INVALID_ARG;
+  if (!is_pow2(p->page_size) || p->page_size > 4096) return SMLA_ERR_INVALID_ARG;
+  if (p->kv_format != SMLA_KV_BF16 && p->kv_format != SMLA_KV_FP8_E4M3) return SMLA_ERR_INVALID_ARG;
+  if (p->index_mode != SMLA_IDX_SLOT && p->index_mode != SMLA_IDX_LOGICAL) return SMLA_ERR_INVALID_ARG;
+  if (p->tiling < SMLA_TILING_AUTO || p->tiling > SMLA_TILING_PAD64) return SMLA_ERR_INVALID_ARG;
+  if (p->num_splits < 0) return SMLA_ERR_INVALID_ARG;
+  if (!std::isfinite(p->softmax_scale)) return SMLA_ERR_INVALID_ARG;
+  if (p->q_stride_h < SMLA_D_QK || p->q_stride_h % 8 || p->q_stride_t < 0 || p->q_stride_t % 8)
+    return SMLA_ERR_INVALID_ARG;
+  if (p->out_stride_h < SMLA_D_V || p->out_stride_h % 8 || p->out_stride_t < 0 || p->out_stride_t % 8)
+    return SMLA_ERR_INVALID_ARG;
+  if (p->lse_stride_t < 0) return SMLA_ERR_INVALID_ARG;
+  if (p->num_tokens > 1 && (p->q_stride_t < (int64_t)p->num_heads * p->q_stride_h - (p->q_stride_h - SMLA_D_QK) ||
+                            p->out_stride_t < (int64_t)p->num_heads * p->out_stride_h - (p->out_stride_h - SMLA_D_V) ||
+                            p->lse_stride_t < p->num_heads))
+    return SMLA_ERR_INVALID_ARG;   // rows of q / out / lse would overlap
+  if (p->num_tokens > 0) {
+    if (p->num_pages < 1) return SMLA_ERR_INVALID_ARG;
+    if (p->num_pages > (int64_t)INT32_MAX / p->page_size) return SMLA_ERR_UNSUPPORTED;
+    if (p->index_mode == SMLA_IDX_LOGICAL) {
+      if (p->num_seqs < 1 || p->max_blocks_per_seq < 1 || p->block_table_stride < p->max_blocks_per_seq)
+        return SMLA_ERR_INVALID_ARG;
+    }
+  }
+  if (p->kv_format == SMLA_KV_FP8_E4M3) return SMLA_ERR_UNSUPPORTED;   // fp8 kernel not built yet
+  return SMLA_OK;
+}
+
+int head_groups_for(const smla_params* p) {
+  if (p->tiling == SMLA_TILING_PAD64) return 4;
+  if (p->num_heads <= 16) return 1;
+  if (p->num_heads <= 32) return 2;
+  return 4;
+}
+
+int splits_for(const smla_params* p, int32_t num_cus, const smla::FwdShape& sh) {
+  if (p->num_splits > 0) return p->num_splits;
+  const int64_t T = p->num_tokens;
+  if (T <= 0 || T >= num_cus) return 1;
+  int64_t s = num_cus / T;
+  // keep at least one tile per row group in every split
+  const int64_t rows_per_wg = (int64_t)sh.tile_rows * sh.row_groups;
+  int64_t smax = p->topk / rows_per_wg;
+  if (smax < 1) smax = 1;
+  if (s > smax) s = smax;
+  if (T * s > SMLA_MAX_SPLIT_UNITS) s = SMLA_MAX_SPLIT_UNITS / T;
+  return s < 1 ? 1 : (int)s;
+}
+
+int make_plan(const smla_params* p, int32_t num_cus, smla_plan* plan) {
+  int rc = check_params(p);
+  if (rc != SMLA_OK) return rc;
+  if (num_cus < 1) return SMLA_ERR_INVALID_ARG;
+  smla::FwdShape sh{};
+  const int hg = head_groups_for(p);
+  if (!smla::fwd_shape(p->kv_format, hg, p->kernel_variant, &sh)) return SMLA_ERR_UNSUPPORTED;
+  const int S = splits_for(p, num_cus, sh);
+  smla_plan pl{};
+  pl.head_groups = sh.head_groups;
+  pl.row_groups = sh.row_groups;
+  pl.tile_rows = sh.tile_rows;
+  pl.stages = sh.stages;
+  pl.threads = sh.threads;
+  pl.lds_bytes = sh.lds_bytes;
+  pl.num_splits = S;
+  pl.units = (int64_t)p->num_tokens * S;
+  pl.grid = (pl.units + 7) / 8 * 8;
+  pl.workspace_bytes = S > 1 ? pl.units * p->num_heads * kPartialFloatsPerHead * 4 : 0;
+  pl.partials_bytes = pl.units * p->num_heads * kPartialFloatsPerHead * 4;
+  pl.num_cus = num_cus;
+  *plan = pl;
+  return SMLA_OK;
+}
+
+std::mutex g_mu;
+int g_cus[256];
+
+int device_cus(int32_t* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return SMLA_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (g_cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
+      return SMLA_ERR_HIP;
+    g_cus[dev] = v;
+  }
+  *cus = g_cus[dev];
+  return SMLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sparse_mla_workspace_size(const smla_params* p) {
+  if (check_params(p) != SMLA_OK) return 0;
+  const int64_t per_unit = (int64_t)p->num_heads * kPartialFloatsPerHead * 4;
+  if (p->num_splits == 0) return (size_t)(SMLA_MAX_SPLIT_UNITS * per_unit);
+  if (p->num_splits == 1) return 0;
+  return (size_t)((int64_t)p->num_tokens * p->num_splits * per_unit);
+}
+
+int sparse_mla_plan_for(const smla_params* p, int32_t num_cus, smla_plan* plan) {
+  if (!plan) return SMLA_ERR_INVALID_ARG;
+  return make_plan(p, num_cus, plan);
+}
+
+int sparse_mla_plan(const smla_params* p, smla_plan* plan) {
+  if (!plan) return SMLA_ERR_INVALID_ARG;
+  int rc = check_params(p);
+  if (rc != SMLA_OK) return rc;
+  int32_t cus = 0;
+  rc = device_cus(&cus);
+  if (rc != SMLA_OK) return rc;
+  return make_plan(p, cus, plan);
+}
+
+}  // extern "C"
+
+namespace {
+
+enum class Mode { kFull, kPartials };
+
+int run(Mode mode, const smla_params* p, const void* q, const void* kv_cache, const int32_t* block_table,
+        const int32_t* token_seq, const int32_t* topk_idx, void* out, float* lse, void* workspace,
+        size_t workspace_bytes, void* stream) {
+  int rc = check_params(p);
+  if (rc != SMLA_OK) return rc;
+  if (p->num_tokens == 0) return SMLA_OK;
+  if (!q || !kv_cache || !topk_idx) return SMLA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(topk_idx, 4)) return SMLA_ERR_INVALID_ARG;
+  if (mode == Mode::kFull && (!out || !lse || !aligned(out, 16) || !aligned(lse, 4))) return SMLA_ERR_INVALID_ARG;
+  if (p->index_mode == SMLA_IDX_LOGICAL) {
+    if (!block_table || !token_seq || !aligned(block_table, 4) || !aligned(token_seq, 4))
+      return SMLA_ERR_INVALID_ARG;
+  }
+  const int64_t per_unit = (int64_t)p->num_heads * kPartialFloatsPerHead * 4;
+  if (p->num_splits > 0 && (mode == Mode::kPartials || p->num_splits > 1)) {
+    // forced split count: the workspace need is known without the device
+    const size_t need = (size_t)((int64_t)p->num_tokens * p->num_splits * per_unit);
+    if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return SMLA_ERR_WORKSPACE_TOO_SMALL;
+  }
+  int32_t cus = 0;
+  rc = device_cus(&cus);
+  if (rc != SMLA_OK) return rc;
+  smla_plan pl{};
+  rc = make_plan(p, cus, &pl);
+  if (rc != SMLA_OK) return rc;
+  const bool partials = (mode == Mode::kPartials) || pl.num_splits > 1;
+  if (partials) {
+    const size_t need = (size_t)(pl.units * per_unit);
+    if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return SMLA_ERR_WORKSPACE_TOO_SMALL;
+  }
+
+  smla::FwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv = static_cast<const uint8_t*>(kv_cache);
+  a.block_table = block_table;
+  a.token_seq = token_seq;
+  a.topk_idx = topk_idx;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.ws_out = partials ? static_cast<float*>(workspace) : nullptr;
+  a.ws_lse = partials ? a.ws_out + pl.units * p->num_heads * SMLA_D_V : nullptr;
+  a.q_st = p->q_stride_t;
+  a.q_sh = p->q_stride_h;
+  a.out_st = p->out_stride_t;
+  a.out_sh = p->out_stride_h;
+  a.lse_st = p->lse_stride_t;
+  a.idx_stride = p->idx_stride;
+  a.bt_stride = p->block_table_stride;
+  a.num_slots = p->num_pages * p->page_size;
+  a.num_pages = p->num_pages;
+  a.units = pl.units;
+  a.T = p->num_tokens;
+  a.h = p->num_heads;
+  a.topk = p->topk;
+  a.num_splits = pl.num_splits;
+  a.page_shift = log2i(p->page_size);
+  a.index_mode = p->index_mode;
+  a.num_seqs = p->num_seqs;
+  a.max_blocks = p->max_blocks_per_seq;
+  a.grid_per_xcd = (int32_t)(pl.grid / 8);
+  a.write_partials = partials ? 1 : 0;
+  a.scale_log2 = p->softmax_scale * 1.44269504088896340736f;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (smla::launch_fwd(a, p->kv_format, pl.head_groups, p->kernel_variant, pl.grid, st) != hipSuccess)
+    return SMLA_ERR_HIP;
+  if (mode == Mode::kFull && pl.num_splits > 1) {
+    smla::CombineArgs c{};
+    c.ws_out = a.ws_out;
+    c.ws_lse = a.ws_lse;
+    c.out = a.out;
+    c.lse = lse;
+    c.out_st = p->out_stride_t;
+    c.out_sh = p->out_stride_h;
+    c.lse_st = p->lse_stride_t;
+    c.T = p->num_tokens;
+    c.h = p->num_heads;
+    c.num_splits = pl.num_splits;
+    if (smla::launch_combine(c, st) != hipSuccess) return SMLA_ERR_HIP;
+  }
+  return SMLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sparse_mla_fwd(const smla_params* p, const void* q, const void* kv_cache, const int32_t* block_table,
+                   const int32_t* token_seq, const int32_t* topk_idx, void* out, float* lse, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return run(Mode::kFull, p, q, kv_cache, block_table, token_seq, topk_idx, out, lse, workspace,
+             workspace_bytes, stream);
+}
+
+int sparse_mla_fwd_partials(const smla_params* p, const void* q, const void* kv_cache,
+                            const int32_t* block_table, const int32_t* token_seq, const int32_t* topk_idx,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return run(Mode::kPartials, p, q, kv_cache, block_table, token_seq, topk_idx, nullptr, nullptr, workspace,
+             workspace_bytes, stream);
+}
+
+int sparse_mla_lse_combine(const float* part_out, const float* part_lse, int32_t num_tokens, int32_t num_splits,
+                           int32_t num_heads, void* out, int64_t out_stride_t, int64_t out_stride_h, float* lse,
+                           int64_t lse_stride_t, void* stream) {
+  if (num_tokens < 0 || num_splits < 1 || num_heads < 1 || num_heads > SMLA_MAX_HEADS) return SMLA_ERR_INVALID_ARG;
+  if (out_stride_h < SMLA_D_V || out_stride_h % 8 || out_stride_t < 0 || out_stride_t % 8 || lse_stride_t < 0)
+    return SMLA_ERR_INVALID_ARG;
+  if (num_tokens > 1 && (out_stride_t < (int64_t)(num_heads - 1) * out_stride_h + SMLA_D_V || lse_stride_t < num_heads))
+    return SMLA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return SMLA_OK;
+  if (!part_out || !part_lse || !out || !lse) return SMLA_ERR_INVALID_ARG;
+  if (!aligned(part_out, 16) || !aligned(part_lse, 4) || !aligned(out, 16) || !aligned(lse, 4))
+    return SMLA_ERR_INVALID_ARG;
+  smla::CombineArgs c{};
+  c.ws_out = part_out;
+  c.ws_lse = part_lse;
+  c.out = static_cast<uint16_t*>(out);
+  c.lse = lse;
+  c.out_st = out_stride_t;
+  c.out_sh = out_stride_h;
+  c.lse_st = lse_stride_t;
+  c.T = num_tokens;
+  c.h = num_heads;
+  c.num_splits = num_splits;
+  if (smla::launch_combine(c, static_cast<hipStream_t>(stream)) != hipSuccess) return SMLA_ERR_HIP;
+  return SMLA_OK;
+}
+
+const char* sparse_mla_status_string(int status) {
+  switch (status) {
+    case SMLA_OK: return "ok";
+    case SMLA_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad size or stride)";
+    case SMLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SMLA_ERR_WORKSPACE_TOO_SMALL: return "workspace missing or smaller than sparse_mla_workspace_size()";
+    case SMLA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

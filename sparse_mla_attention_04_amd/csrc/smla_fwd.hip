@@ -1,0 +1,541 @@
+// Sparse MLA forward over top-k selected cache rows, CDNA4 (gfx950) kernels.
+//
+// What is computed: for each query row t, attention of its h heads over the
+// cache rows its index list names, all heads sharing the same 576-wide rows
+// (MQA / absorbed form; prhub report on vLLM PR #55738, "Motivation"), with
+// the output in the 512-dim latent space and an fp32 log-sum-exp per head
+// (vLLM PR #60220, "Claims" and "Details").
+//
+// Design (one work-group = one query row, or one KV split of it):
+//   * index compaction: the row's entries are translated to physical rows
+//     (block table in LOGICAL mode), -1 / out-of-range entries dropped, and
+//     the surviving rows stored in order in LDS;
+//   * gather: rows are copied HBM -> LDS with direct-to-LDS 16-byte loads
+//     (global_load_lds_dwordx4), a ring of `NST` tiles per row group, issued
+//     and waited on by hand so several tiles stay in flight; eight lanes
+//     fetch one 128-byte line of a row, the 16-byte chunks of a line being
+//     XOR-swizzled so MFMA operand reads are free of LDS bank conflicts;
+//   * scores: S^T = K . Q^T on v_mfma_f32_16x16x32_bf16 (K from LDS, the
+//     row's queries for 16 heads held in registers), so each lane ends up
+//     owning one head's scores;
+//   * online softmax in base 2 with wave-level reductions (max over the four
+//     lanes that share a head);
+//   * P.V: O^T += V^T . P^T on MFMA, V^T read straight from the same LDS
+//     tile with ds_read_b64_tr_b16 (the transposing LDS read of gfx950);
+//   * waves that split the rows of one query are merged through LDS at the
+//     end; a split work-group writes its fp32 partial (normalised output
+//     and lse) to the caller's workspace instead, and a second kernel merges
+//     the splits by their lse (the fp32 split-KV path of PR #60220,
+//     "Overview"/"Limitations", with the buffer owned by the caller).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "smla_internal.h"
+
+namespace smla {
+namespace {
+
+#define LDS_AS __attribute__((address_space(3)))
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+constexpr int D_QK = 576;
+constexpr int D_V = 512;
+constexpr int ROW_BYTES = D_QK * 2;     // bf16 cache row
+constexpr int LIST_CAP = 2048;          // index entries compacted per pass
+constexpr float NEG_INF = -__builtin_inff();
+constexpr float LN2 = 0.69314718055994530942f;
+
+template <int HG_, int NRG_, int RT_, int NST_>
+struct Shape {
+  static constexpr int HG = HG_;            // 16-head groups (waves per row group)
+  static constexpr int NRG = NRG_;          // row groups (independent KV row streams)
+  static constexpr int RT = RT_;            // rows per tile
+  static constexpr int NST = NST_;          // tiles in flight per row group
+  static constexpr int NW = HG * NRG;       // waves
+  static constexpr int NTHR = NW * 64;
+  static constexpr int NF = RT / 16;        // 16-row score fragments per tile
+  static constexpr int NRH = RT / 8;        // 8-row DMA groups per tile
+  static constexpr int RH_PER_WAVE = NRH / HG;
+  static constexpr int PER = 9 * RH_PER_WAVE;   // DMA instructions per wave per tile
+  static constexpr int TILE_BYTES = RT * ROW_BYTES;
+  static constexpr int RING_BYTES = NRG * NST * TILE_BYTES;
+  static constexpr int LIST_OFF = RING_BYTES;
+  static constexpr int CNT_OFF = LIST_OFF + LIST_CAP * 4;
+  static constexpr int STAT_OFF = CNT_OFF + 64;
+  static constexpr int LDS_BYTES = STAT_OFF + NW * 16 * 2 * 4;
+  static constexpr int EPT = LIST_CAP / NTHR;   // index entries per thread per pass
+  static constexpr bool SYNC = HG > 1;          // waves share tiles -> barrier per tile
+  static_assert(RT == 16 || RT == 32, "tile rows");
+  static_assert(NRH % HG == 0, "DMA groups must split evenly over the waves of a row group");
+  static_assert((NST - 1) * PER <= 63, "vmcnt holds at most 63 outstanding loads");
+  static_assert(NW * 32 * 64 * 16 <= RING_BYTES, "epilogue staging must fit in the ring");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(LIST_CAP % NTHR == 0, "compaction split");
+};
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const LDS_AS void*)p;
+}
+
+// One 64 x 16-byte direct-to-LDS gather: lane l reads 16 bytes at
+// gaddr + OFF and writes them to LDS at m0 + OFF + 16 * l.
+template <int OFF>
+__device__ __forceinline__ void dma16(const void* gaddr, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2"
+               :
+               : "v"(gaddr), "s"(__builtin_amdgcn_readfirstlane(m0)), "n"(OFF)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// Wait until at most pend * PER of this wave's gathers are outstanding.
+template <int PER, int NST>
+__device__ __forceinline__ void wait_tiles(int pend) {
+  if (pend <= 0) { wait_vm<0>(); return; }
+  if constexpr (NST > 2) {
+    if (pend == 1) { wait_vm<PER>(); return; }
+    if constexpr (NST > 3) {
+      if (pend == 2) { wait_vm<2 * PER>(); return; }
+      if constexpr (NST > 4) {
+        if (pend == 3) { wait_vm<3 * PER>(); return; }
+      }
+    }
+  }
+  // pend >= NST - 1: nothing newer than (NST - 1) tiles can be pending
+  wait_vm<(NST - 1) * PER>();
+}
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" : : : "memory"); }
+
+__device__ __forceinline__ float wave_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  __bf16 b = (__bf16)x;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// Translate one index entry to a physical cache row; -1 when skipped.
+__device__ __forceinline__ int translate(const FwdArgs& a, int j, int seq_ok, int64_t bt_row) {
+  if (j < 0) return -1;
+  if (a.index_mode == 0) return (j < a.num_slots) ? j : -1;
+  if (!seq_ok) return -1;
+  const int blk = j >> a.page_shift;
+  if (blk >= a.max_blocks) return -1;
+  const int page = a.block_table[bt_row + blk];
+  if (page < 0 || page >= a.num_pages) return -1;
+  return (page << a.page_shift) | (j & ((1 << a.page_shift) - 1));
+}
+
+template <class S>
+__global__ void __launch_bounds__(S::NTHR, 1) smla_fwd_bf16(FwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S::LDS_BYTES];
+  int* list = reinterpret_cast<int*>(smem + S::LIST_OFF);
+  int* wcnt = reinterpret_cast<int*>(smem + S::CNT_OFF);
+  float* stat = reinterpret_cast<float*>(smem + S::STAT_OFF);
+  const LDS_AS uint8_t* lds = (const LDS_AS uint8_t*)smem;
+  const uint32_t ring0 = lds_addr(smem);
+
+  // XCD-aware unit mapping: consecutive units share an XCD (and its L2).
+  const int b = blockIdx.x;
+  const int64_t unit = (int64_t)(b & 7) * a.grid_per_xcd + (b >> 3);
+  if (unit >= a.units) return;
+  const int S_ = a.num_splits;
+  const int t = (int)(unit / S_);
+  const int sp = (int)(unit - (int64_t)t * S_);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int hg = wave % S::HG, rg = wave / S::HG;
+  const int g4 = lane >> 4, n = lane & 15;
+
+  // ---- queries of this wave's 16 heads, in the MFMA B-operand layout:
+  //      lane (g4, n) holds head hg*16+n, dims 32*kk + 8*g4 .. +7
+  bf16x8 qb[18];
+  {
+    const int head = hg * 16 + n;
+    if (head < a.h) {
+      const uint16_t* qp = a.q + (int64_t)t * a.q_st + (int64_t)head * a.q_sh + 8 * g4;
+#pragma unroll
+      for (int kk = 0; kk < 18; ++kk) qb[kk] = *reinterpret_cast<const bf16x8*>(qp + 32 * kk);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 18; ++kk) qb[kk] = bf16x8{};
+    }
+  }
+
+  // ---- per-lane LDS offsets inside a tile
+  // tile layout: position(r, c) = (c / 8) * RT * 8 + r * 8 + ((c % 8) ^ ((r >> 1) & 7)), 16 B each
+  uint32_t kofs[S::NF][2];     // K operand: row 16f+n, chunk 4*kk+g4
+  uint32_t vofs[S::NF][4];     // V^T operand (transposing read): row 16f+4*g4+(n>>2), dims 4*(n&3)
+#pragma unroll
+  for (int f = 0; f < S::NF; ++f) {
+    const int r = 16 * f + n;
+    const int sw = (r >> 1) & 7;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) kofs[f][p] = (uint32_t)(r * 8 + ((4 * p + g4) ^ sw)) * 16u;
+    const int rv = 16 * f + 4 * g4 + (n >> 2);
+    const int swv = (rv >> 1) & 7;
+    const int cq = n & 3;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      vofs[f][p] = (uint32_t)(rv * 8 + ((2 * p + (cq >> 1)) ^ swv)) * 16u + (uint32_t)(cq & 1) * 8u;
+  }
+
+  f32x4 o[32];
+#pragma unroll
+  for (int f = 0; f < 32; ++f) o[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = NEG_INF, l_run = 0.f;
+
+  // ---- index range of this split
+  const int64_t c0 = (int64_t)a.topk * sp / S_;
+  const int64_t c1 = (int64_t)a.topk * (sp + 1) / S_;
+  const int32_t* idx_row = a.topk_idx + (int64_t)t * a.idx_stride;
+  int seq = 0, seq_ok = 1;
+  int64_t bt_row = 0;
+  if (a.index_mode == 1) {
+    seq = a.token_seq[t];
+    seq_ok = (seq >= 0 && seq < a.num_seqs);
+    bt_row = seq_ok ? (int64_t)seq * a.bt_stride : 0;
+  }
+
+  // make the compiler's wait for the query loads happen before any gather is in flight
+#pragma unroll
+  for (int kk = 0; kk < 18; ++kk) asm volatile("" : : "v"(qb[kk]));
+
+  for (int64_t cs = c0; cs < c1; cs += LIST_CAP) {
+    const int64_t ce = (cs + LIST_CAP < c1) ? cs + LIST_CAP : c1;
+    // ---- compaction: thread tid owns entries cs + tid*EPT .. +EPT-1 (order preserved)
+    int sl[S::EPT];
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < S::EPT; ++i) {
+      const int64_t e = cs + (int64_t)tid * S::EPT + i;
+      int s = -1;
+      if (e < ce) s = translate(a, idx_row[e], seq_ok, bt_row);
+      sl[i] = s;
+      cnt += (s >= 0);
+    }
+    int incl = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += v;
+    }
+    if (lane == 63) wcnt[wave] = incl;
+    __syncthreads();
+    int base = 0, n_valid = 0;
+#pragma unroll
+    for (int w = 0; w < S::NW; ++w) {
+      const int c = wcnt[w];
+      base += (w < wave) ? c : 0;
+      n_valid += c;
+    }
+    int pos = base + incl - cnt;
+#pragma unroll
+    for (int i = 0; i < S::EPT; ++i) {
+      if (sl[i] >= 0) { list[pos] = sl[i]; ++pos; }
+    }
+    __syncthreads();
+
+    // ---- tiles: tile i belongs to row group i % NRG
+    const int ntile = (n_valid + S::RT - 1) / S::RT;
+    const int nt_rg = (ntile > rg) ? (ntile - rg + S::NRG - 1) / S::NRG : 0;
+    const int nit = S::SYNC ? (ntile + S::NRG - 1) / S::NRG : nt_rg;
+
+    auto tile_lds = [&](int it) -> uint32_t {
+      return ring0 + (uint32_t)((rg * S::NST + (it % S::NST)) * S::TILE_BYTES);
+    };
+    auto issue = [&](int it) {
+      const int tstart = (rg + S::NRG * it) * S::RT;
+      const uint32_t tl = tile_lds(it);
+#pragma unroll
+      for (int k = 0; k < S::RH_PER_WAVE; ++k) {
+        const int rh = hg + k * S::HG;
+        const int r = 8 * rh + (lane >> 3);
+        int li = tstart + r;
+        li = (li < n_valid) ? li : n_valid - 1;           // tail rows repeat the last valid row
+        const int slot = list[li];
+        const int q = (lane & 7) ^ ((r >> 1) & 7);
+        const uint8_t* g = a.kv + (int64_t)slot * ROW_BYTES + q * 16;
+        const uint32_t mb = tl + (uint32_t)rh * 1024u;
+        // line L of the row lands at tile position L*RT*8 + rh*64 + lane
+        dma16<0 * 128>(g, mb + 0 * (S::RT * 128 - 128));
+        dma16<1 * 128>(g, mb + 1 * (S::RT * 128 - 128));
+        dma16<2 * 128>(g, mb + 2 * (S::RT * 128 - 128));
+        dma16<3 * 128>(g, mb + 3 * (S::RT * 128 - 128));
+        dma16<4 * 128>(g, mb + 4 * (S::RT * 128 - 128));
+        dma16<5 * 128>(g, mb + 5 * (S::RT * 128 - 128));
+        dma16<6 * 128>(g, mb + 6 * (S::RT * 128 - 128));
+        dma16<7 * 128>(g, mb + 7 * (S::RT * 128 - 128));
+        dma16<8 * 128>(g, mb + 8 * (S::RT * 128 - 128));
+      }
+    };
+    auto compute = [&](int it) {
+      const int tstart = (rg + S::NRG * it) * S::RT;
+      const uint32_t toff = tile_lds(it) - ring0;
+      const LDS_AS uint8_t* tp = lds + toff;
+      // scores S^T[row][head] for this wave's 16 heads
+      f32x4 sc[S::NF];
+#pragma unroll
+      for (int f = 0; f < S::NF; ++f) {
+        f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+#pragma unroll
+        for (int kk = 0; kk < 18; kk += 2) {
+          const bf16x8 k0 = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[f][0] + (kk >> 1) * S::RT * 128);
+          const bf16x8 k1 = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[f][1] + (kk >> 1) * S::RT * 128);
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[kk], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[kk + 1], acc1, 0, 0, 0);
+        }
+        sc[f] = acc0 + acc1;
+      }
+      // online softmax (base 2); lane owns head n, rows 16f + 4*g4 + j
+      const int left = n_valid - tstart;
+      float x[S::NF][4];
+      float mx = NEG_INF;
+#pragma unroll
+      for (int f = 0; f < S::NF; ++f)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 16 * f + 4 * g4 + j;
+          const float v = sc[f][j] * a.scale_log2;
+          x[f][j] = (r < left) ? v : NEG_INF;
+          mx = fmaxf(mx, x[f][j]);
+        }
+      mx = fmaxf(mx, wave_xor(mx, 16));
+      mx = fmaxf(mx, wave_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      float psum = 0.f;
+      float pv[S::NF][4];
+#pragma unroll
+      for (int f = 0; f < S::NF; ++f)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          pv[f][j] = fast_exp2(x[f][j] - m_new);
+          psum += pv[f][j];
+        }
+      l_run = l_run * alpha + psum;
+#pragma unroll
+      for (int f = 0; f < 32; ++f) o[f] *= alpha;
+      // P.V
+      if constexpr (S::RT == 16) {
+        bf16x4 pb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pb[j] = (__bf16)pv[0][j];
+#pragma unroll
+        for (int f = 0; f < 32; ++f) {
+          const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (LDS_AS bf16x4*)(tp + vofs[0][f & 3] + (f >> 2) * S::RT * 128));
+          o[f] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[f], 0, 0, 0);
+        }
+      } else {
+        bf16x8 pb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          pb[j] = (__bf16)pv[0][j];
+          pb[4 + j] = (__bf16)pv[1][j];
+        }
+#pragma unroll
+        for (int f = 0; f < 32; ++f) {
+          const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (LDS_AS bf16x4*)(tp + vofs[0][f & 3] + (f >> 2) * S::RT * 128));
+          const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (LDS_AS bf16x4*)(tp + vofs[1][f & 3] + (f >> 2) * S::RT * 128));
+          const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+          o[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[f], 0, 0, 0);
+        }
+      }
+    };
+
+    // ---- the pipeline
+    int iss = 0;
+#pragma unroll
+    for (int st = 0; st < S::NST - 1; ++st) {
+      if (iss < nit) {
+        if (iss < nt_rg) issue(iss);
+        ++iss;
+      }
+    }
+    for (int it = 0; it < nit; ++it) {
+      if constexpr (!S::SYNC) {
+        if (iss < nit) {
+          if (iss < nt_rg) issue(iss);
+          ++iss;
+        }
+      }
+      const int real = (iss < nt_rg) ? iss : nt_rg;
+      wait_tiles<S::PER, S::NST>(real - (it + 1));
+      if constexpr (S::SYNC) {
+        lds_barrier();
+        if (iss < nit) {
+          if (iss < nt_rg) issue(iss);
+          ++iss;
+        }
+      }
+      if (it < nt_rg) compute(it);
+    }
+    wait_vm<0>();
+    __syncthreads();   // the list is rewritten by the next pass
+  }
+
+  // ---- epilogue: merge the row groups of each head group, normalise, write
+  float l_tot = l_run + wave_xor(l_run, 16);
+  l_tot += wave_xor(l_tot, 32);
+  __syncthreads();
+  if (lane < 16) {
+    stat[(wave * 16 + lane) * 2 + 0] = m_run;
+    stat[(wave * 16 + lane) * 2 + 1] = l_tot;
+  }
+  {
+    f32x4* ost = reinterpret_cast<f32x4*>(smem) + (size_t)wave * 32 * 64;
+#pragma unroll
+    for (int f = 0; f < 32; ++f) ost[f * 64 + lane] = o[f];
+  }
+  __syncthreads();
+  const bool split = a.write_partials != 0;
+  for (int item = tid; item < a.h * 64; item += S::NTHR) {
+    const int head = item >> 6, c = item & 63;
+    const int hgi = head >> 4, nn = head & 15;
+    float M = NEG_INF;
+#pragma unroll
+    for (int r = 0; r < S::NRG; ++r) M = fmaxf(M, stat[((r * S::HG + hgi) * 16 + nn) * 2]);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
+    if (M != NEG_INF) {
+#pragma unroll
+      for (int r = 0; r < S::NRG; ++r) {
+        const int w = r * S::HG + hgi;
+        const float fct = fast_exp2(stat[(w * 16 + nn) * 2] - M);
+        L += fct * stat[(w * 16 + nn) * 2 + 1];
+        // dims 8c..8c+7 = fragment c/2, lanes (2*(c&1) + {0,1})*16 + nn, j = 0..3
+        const f32x4* ost = reinterpret_cast<const f32x4*>(smem) + (size_t)w * 32 * 64 + (c >> 1) * 64;
+        const f32x4 v0 = ost[(2 * (c & 1) + 0) * 16 + nn];
+        const f32x4 v1 = ost[(2 * (c & 1) + 1) * 16 + nn];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[j] += fct * v0[j];
+          acc[4 + j] += fct * v1[j];
+        }
+      }
+    }
+    const bool empty = !(L > 0.f);
+    const float inv = empty ? 0.f : 1.f / L;
+    const float lse_v = empty ? NEG_INF : (M + __log2f(L)) * LN2;
+    if (!split) {
+      u32x4 pk;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        pk[j] = (uint32_t)f32_to_bf16_bits(acc[2 * j] * inv) |
+                ((uint32_t)f32_to_bf16_bits(acc[2 * j + 1] * inv) << 16);
+      *reinterpret_cast<u32x4*>(a.out + (int64_t)t * a.out_st + (int64_t)head * a.out_sh + 8 * c) = pk;
+      if (c == 0) a.lse[(int64_t)t * a.lse_st + head] = lse_v;
+    } else {
+      float* wo = a.ws_out + ((unit * a.h + head) * D_V) + 8 * c;
+      f32x4 w0, w1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        w0[j] = acc[j] * inv;
+        w1[j] = acc[4 + j] * inv;
+      }
+      reinterpret_cast<f32x4*>(wo)[0] = w0;
+      reinterpret_cast<f32x4*>(wo)[1] = w1;
+      if (c == 0) a.ws_lse[unit * a.h + head] = lse_v;
+    }
+  }
+}
+
+// Merge the KV splits of each query row by their lse, in split order.
+__global__ void __launch_bounds__(256) smla_lse_combine(CombineArgs a) {
+  const int t = blockIdx.x;
+  const int S_ = a.num_splits;
+  for (int item = threadIdx.x; item < a.h * 64; item += 256) {
+    const int head = item >> 6, c = item & 63;
+    float M = NEG_INF;
+    for (int s = 0; s < S_; ++s) M = fmaxf(M, a.ws_lse[((int64_t)t * S_ + s) * a.h + head]);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
+    if (M != NEG_INF) {
+      for (int s = 0; s < S_; ++s) {
+        const int64_t u = (int64_t)t * S_ + s;
+        const float ls = a.ws_lse[u * a.h + head];
+        const float w = fast_exp2((ls - M) * 1.44269504088896340736f);
+        L += w;
+        const f32x4* src = reinterpret_cast<const f32x4*>(a.ws_out + (u * a.h + head) * D_V + 8 * c);
+        const f32x4 v0 = src[0], v1 = src[1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[j] += w * v0[j];
+          acc[4 + j] += w * v1[j];
+        }
+      }
+    }
+    const bool empty = !(L > 0.f);
+    const float inv = empty ? 0.f : 1.f / L;
+    u32x4 pk;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      pk[j] = (uint32_t)f32_to_bf16_bits(acc[2 * j] * inv) |
+              ((uint32_t)f32_to_bf16_bits(acc[2 * j + 1] * inv) << 16);
+    *reinterpret_cast<u32x4*>(a.out + (int64_t)t * a.out_st + (int64_t)head * a.out_sh + 8 * c) = pk;
+    if (c == 0) a.lse[(int64_t)t * a.lse_st + head] = empty ? NEG_INF : M + __logf(L);
+  }
+}
+
+// Kernel variants: (head groups, row groups, tile rows, stages).
+using V_H1_A = Shape<1, 4, 16, 2>;
+using V_H1_B = Shape<1, 2, 16, 4>;
+using V_H2_A = Shape<2, 2, 32, 2>;
+using V_H2_B = Shape<2, 1, 32, 4>;
+using V_H4_A = Shape<4, 1, 32, 4>;
+
+template <class S>
+FwdShape shape_of() {
+  return FwdShape{S::HG, S::NRG, S::RT, S::NST, S::NTHR, S::LDS_BYTES};
+}
+
+template <class S>
+hipError_t launch_one(const FwdArgs& a, int64_t grid, hipStream_t stream) {
+  hipLaunchKernelGGL(smla_fwd_bf16<S>, dim3((unsigned)grid), dim3(S::NTHR), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool fwd_shape(int kv_format, int head_groups, int variant, FwdShape* shape) {
+  if (kv_format != 0) return false;
+  switch (head_groups) {
+    case 1: *shape = variant == 1 ? shape_of<V_H1_B>() : shape_of<V_H1_A>(); return variant <= 1;
+    case 2: *shape = variant == 1 ? shape_of<V_H2_B>() : shape_of<V_H2_A>(); return variant <= 1;
+    case 4: *shape = shape_of<V_H4_A>(); return variant == 0;
+    default: return false;
+  }
+}
+
+hipError_t launch_fwd(const FwdArgs& a, int kv_format, int head_groups, int variant, int64_t grid,
+                      hipStream_t stream) {
+  if (kv_format != 0) return hipErrorInvalidValue;
+  switch (head_groups) {
+    case 1: return variant == 1 ? launch_one<V_H1_B>(a, grid, stream) : launch_one<V_H1_A>(a, grid, stream);
+    case 2: return variant == 1 ? launch_one<V_H2_B>(a, grid, stream) : launch_one<V_H2_A>(a, grid, stream);
+    case 4: return launch_one<V_H4_A>(a, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(smla_lse_combine, dim3((unsigned)a.T), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace smla

@@ -1,0 +1,52 @@
+// Internal interface between the C-ABI host code and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smla {
+
+// Everything a forward launch needs, passed by value as the kernel argument.
+struct FwdArgs {
+  const uint16_t* q;          // bf16 [T, h, 576] (strided)
+  const uint8_t* kv;          // cache pool base
+  const int32_t* block_table; // LOGICAL mode
+  const int32_t* token_seq;   // LOGICAL mode
+  const int32_t* topk_idx;    // int32 [T, idx_stride]
+  uint16_t* out;              // bf16 [T, h, 512] (strided)
+  float* lse;                 // fp32 [T, h] (strided)
+  float* ws_out;              // fp32 [units, h, 512] split partials
+  float* ws_lse;              // fp32 [units, h]
+  int64_t q_st, q_sh, out_st, out_sh, lse_st, idx_stride, bt_stride;
+  int64_t num_slots;          // num_pages * page_size (<= INT32_MAX)
+  int64_t num_pages;
+  int64_t units;              // T * num_splits
+  int32_t T, h, topk, num_splits;
+  int32_t page_shift, index_mode, num_seqs, max_blocks;
+  int32_t grid_per_xcd;       // launched work-groups / 8
+  int32_t write_partials;     // 1: write fp32 partials to ws_out / ws_lse instead of out / lse
+  float scale_log2;           // softmax_scale * log2(e)
+};
+
+struct CombineArgs {
+  const float* ws_out;
+  const float* ws_lse;
+  uint16_t* out;
+  float* lse;
+  int64_t out_st, out_sh, lse_st;
+  int32_t T, h, num_splits;
+};
+
+// Pipeline shape of one forward kernel instantiation.
+struct FwdShape {
+  int head_groups, row_groups, tile_rows, stages, threads, lds_bytes;
+};
+
+// Shape of kernel `variant` for `head_groups`; returns false when no such kernel exists.
+bool fwd_shape(int kv_format, int head_groups, int variant, FwdShape* shape);
+
+// Launches; return a hipError_t.
+hipError_t launch_fwd(const FwdArgs& a, int kv_format, int head_groups, int variant, int64_t grid,
+                      hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+}  // namespace smla

@@ -1,0 +1,133 @@
+"""C-ABI checks that need no GPU: the library loads, exports what the header
+declares, and rejects bad arguments on the host before touching a device.
+
+Only argument combinations that fail validation are passed to the compute
+entry points here, so no test in this file can launch a kernel, with or
+without a GPU present."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_mla_attention_04_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_mla.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^[a-z_ ]+\**\s*\**(sparse_mla_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_exports_all_loaded():
+    names = _declared_functions()
+    assert set(names) == set(B.EXPORTS), names
+    L = B.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _params(**kw):
+    base = dict(num_tokens=4, num_heads=8, topk=64, num_pages=8, num_seqs=1, max_blocks_per_seq=8)
+    base.update(kw)
+    return B.make_params(**base)
+
+
+def _fwd(p, q=16, kv=16, bt=16, ts=16, idx=16, out=16, lse=16, ws=None, ws_bytes=0):
+    """Call sparse_mla_fwd with fake (never dereferenced) pointer values."""
+    L = B.lib()
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return L.sparse_mla_fwd(ctypes.byref(p), v(q), v(kv), v(bt), v(ts), v(idx), v(out), v(lse), v(ws),
+                            ws_bytes, None)
+
+
+def test_zero_tokens_is_noop():
+    assert _fwd(_params(num_tokens=0), q=None, kv=None, bt=None, ts=None, idx=None, out=None, lse=None) == B.SMLA_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_heads=0), B.SMLA_ERR_INVALID_ARG),
+    (dict(num_heads=65), B.SMLA_ERR_UNSUPPORTED),
+    (dict(topk=0), B.SMLA_ERR_INVALID_ARG),
+    (dict(topk=64, idx_stride=63), B.SMLA_ERR_INVALID_ARG),
+    (dict(page_size=48), B.SMLA_ERR_INVALID_ARG),
+    (dict(page_size=8192), B.SMLA_ERR_INVALID_ARG),
+    (dict(num_tokens=-1), B.SMLA_ERR_INVALID_ARG),
+    (dict(num_pages=0), B.SMLA_ERR_INVALID_ARG),
+    (dict(num_splits=-2), B.SMLA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), B.SMLA_ERR_INVALID_ARG),
+    (dict(q_strides=(8 * 576, 570)), B.SMLA_ERR_INVALID_ARG),
+    (dict(q_strides=(8 * 576 + 4, 576)), B.SMLA_ERR_INVALID_ARG),
+    (dict(out_strides=(512, 512)), B.SMLA_ERR_INVALID_ARG),          # rows would overlap
+    (dict(lse_stride=4), B.SMLA_ERR_INVALID_ARG),
+    (dict(num_seqs=0), B.SMLA_ERR_INVALID_ARG),
+    (dict(max_blocks_per_seq=4, block_table_stride=3), B.SMLA_ERR_INVALID_ARG),
+    (dict(kernel_variant=-1), B.SMLA_ERR_INVALID_ARG),
+])
+def test_bad_params_rejected(kw, code):
+    assert _fwd(_params(**kw)) == code
+    assert B.workspace_size(_params(**kw)) == 0
+
+
+def test_bad_pointers_rejected():
+    p = _params()
+    assert _fwd(p, q=None) == B.SMLA_ERR_INVALID_ARG
+    assert _fwd(p, out=None) == B.SMLA_ERR_INVALID_ARG
+    assert _fwd(p, q=24) == B.SMLA_ERR_INVALID_ARG          # not 16-B aligned
+    assert _fwd(p, out=40) == B.SMLA_ERR_INVALID_ARG
+    assert _fwd(p, idx=18) == B.SMLA_ERR_INVALID_ARG
+    assert _fwd(p, bt=None) == B.SMLA_ERR_INVALID_ARG       # LOGICAL mode needs the block table
+    assert _fwd(p, ts=None) == B.SMLA_ERR_INVALID_ARG
+
+
+def test_forced_split_needs_workspace():
+    p = _params(num_splits=3)
+    need = 4 * 3 * 8 * 513 * 4
+    assert B.workspace_size(p) == need
+    assert _fwd(p, ws=None) == B.SMLA_ERR_WORKSPACE_TOO_SMALL
+    assert _fwd(p, ws=16, ws_bytes=need - 4) == B.SMLA_ERR_WORKSPACE_TOO_SMALL
+    assert _fwd(p, ws=8, ws_bytes=need) == B.SMLA_ERR_WORKSPACE_TOO_SMALL   # misaligned
+
+
+def test_workspace_size_independent_of_tokens():
+    a = B.workspace_size(_params(num_tokens=1))
+    b = B.workspace_size(_params(num_tokens=100000))
+    assert a == b == 1024 * 8 * 513 * 4
+    assert B.workspace_size(_params(num_splits=1)) == 0
+
+
+def test_plan_for_is_pure_and_splits_small_batches():
+    # decode-sized batch: 32 rows on 256 CUs -> 8 KV splits, 256 work-groups
+    p = _params(num_tokens=32, topk=2048, num_pages=8192, num_seqs=32, max_blocks_per_seq=256)
+    pl = B.plan(p, num_cus=256)
+    assert pl.num_splits == 8 and pl.units == 256 and pl.grid == 256 and pl.head_groups == 1
+    assert pl.workspace_bytes == 256 * 8 * 513 * 4 <= B.workspace_size(p)
+    # large batch: unsplit
+    pl = B.plan(_params(num_tokens=4096, topk=2048), num_cus=256)
+    assert pl.num_splits == 1 and pl.workspace_bytes == 0 and pl.grid == 4096
+    # head tiles
+    assert B.plan(_params(num_heads=32), num_cus=256).head_groups == 2
+    assert B.plan(_params(num_heads=64), num_cus=256).head_groups == 4
+    assert B.plan(_params(num_heads=8, tiling="pad64"), num_cus=256).head_groups == 4
+    # grid is a multiple of 8 (XCD-aware mapping)
+    assert B.plan(_params(num_tokens=1001, topk=64), num_cus=256).grid == 1008
+
+
+def test_lse_combine_validation():
+    L = B.lib()
+    c = lambda *a: L.sparse_mla_lse_combine(*a)
+    v = ctypes.c_void_p
+    assert c(None, None, 0, 2, 8, None, 8 * 512, 512, None, 8, None) == B.SMLA_OK
+    assert c(v(16), v(16), 4, 0, 8, v(16), 8 * 512, 512, v(16), 8, None) == B.SMLA_ERR_INVALID_ARG
+    assert c(v(16), v(16), 4, 2, 65, v(16), 65 * 512, 512, v(16), 65, None) == B.SMLA_ERR_INVALID_ARG
+    assert c(None, v(16), 4, 2, 8, v(16), 8 * 512, 512, v(16), 8, None) == B.SMLA_ERR_INVALID_ARG
+    assert c(v(16), v(16), 4, 2, 8, v(24), 8 * 512, 512, v(16), 8, None) == B.SMLA_ERR_INVALID_ARG
+
+
+def test_status_strings():
+    for s in range(5):
+        assert B.status_string(s)
+    assert "unknown" in B.status_string(99)
