@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse MLA forward (top-k = 2048) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload c2_decode]
+
+A step is one sparse_mla_fwd call over one synthetic batch (index
+compaction + gather + QK^T + softmax + PV + split merge when the plan splits).
+Inputs are resident in HBM before timing starts.  K steps are timed with HIP
+events on the stream the library launches on, bracketed by device syncs.
+Prints ONE JSON line: throughput in query-tokens/s, the dominant kernel's
+roofline (per-launch durations from events around each launch), and the CPU
+oracle timed on a bounded sample of the same workload on this host.
+
+Workloads (synthetic, seeded; `--workload`):
+  c2_decode (default)  32 rows x 1 query, h=8, 16384-token contexts
+  c1_tiny              64 rows, h=8, topk=128
+  c3_h{8,16,32,64}     4096 rows over 8 x (8192 + 512) tokens; suffix _pad64 for the padded tiling
+  c4_long_prefill      16384 rows, h=64, 65536-token history, locality-biased indices
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse MLA fwd: query-tokens/s + gathered-KV GB/s & MFMA % of peak, topk=2048"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="c2_decode")
+    ap.add_argument("--splits", type=int, default=0, help="0 = automatic plan")
+    ap.add_argument("--variant", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cold-launches", type=int, default=50)
+    return ap.parse_args()
+
+
+def workload(name):
+    from sparse_mla_attention_04_amd import inputs as G
+    tiling = "native"
+    if name.endswith("_pad64"):
+        tiling = "pad64"
+        name = name[:-len("_pad64")]
+    if name.startswith("c3_h"):
+        h = int(name[len("c3_h"):])
+        case = G.make_config("c3_sweep").with_heads(h)
+        return case, tiling, "c3_sweep"
+    if name in ("c1_tiny", "c2_decode", "c4_long_prefill", "c5_fp8"):
+        return G.make_config(name), tiling, name
+    raise SystemExit("unknown workload %s" % name)
+
+
+def algorithmic_counts(case):
+    """Valid (gathered) rows per call, from the index lists as the library sees them."""
+    idx = case.topk_idx[:, :case.topk]
+    P = case.page_size
+    valid = idx >= 0
+    j = np.where(valid, idx, 0).astype(np.int64)
+    blk = j // P
+    valid &= blk < case.block_table.shape[1]
+    page = case.block_table[case.token_seq[:, None], np.minimum(blk, case.block_table.shape[1] - 1)]
+    valid &= (page >= 0) & (page < case.num_pages)
+    return int(valid.sum())
+
+
+def cpu_baseline(case, seconds):
+    """The oracle, as it stands, on a bounded sample of the workload's rows."""
+    from oracle import sparse_mla_oracle as O
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        threads = 1
+    T = case.num_tokens
+    rng = np.random.default_rng(0)
+    order = rng.permutation(T)
+    kw = dict(topk=case.topk, scale=case.scale, kv_format=case.kv_format, page_size=case.page_size,
+              index_mode="logical", block_table=case.block_table, token_seq=case.token_seq)
+    done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        rows = [int(order[(done + i) % T]) for i in range(8)]
+        O.sparse_mla_forward(case.q, case.kv, case.topk_idx, rows=rows, **kw)
+        done += len(rows)
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": "%d query rows (random order, cycling over all %d rows of the workload) in %.1f s, "
+                      "numpy fp64 oracle" % (done, T, el)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the sparse MLA forward on a single "
+              "MI355X (no collectives); --gpus %d is not supported." % args.gpus, flush=True)
+        sys.exit(2)
+    import torch
+    from sparse_mla_attention_04_amd import binding as B
+    from sparse_mla_attention_04_amd.inputs import DeviceCase as Dev
+
+    case, tiling, wl_name = workload(args.workload)
+    dev = Dev(case)
+    T, h = case.num_tokens, case.num_heads
+    q = dev.q[:, :h, :]
+    out = torch.empty((T, h, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, h), dtype=torch.float32, device="cuda")
+    p = B.params_for(q, dev.kv, dev.idx, out, lse, topk=case.topk, scale=case.scale, page_size=case.page_size,
+                     kv_format=case.kv_format, block_table=dev.bt, token_seq=dev.ts, tiling=tiling,
+                     num_splits=args.splits, kernel_variant=args.variant)
+    pl = B.plan(p)
+    ws = B.workspace_for(p, "cuda")
+    pws = torch.empty(max(16, pl.partials_bytes), dtype=torch.uint8, device="cuda")
+
+    def step():
+        B.fwd(q, dev.kv, dev.idx, out, lse, topk=case.topk, scale=case.scale, workspace=ws,
+              block_table=dev.bt, token_seq=dev.ts, params=p)
+
+    def kernel_only():
+        if pl.num_splits > 1:
+            B.fwd_partials(q, dev.kv, dev.idx, pws, topk=case.topk, scale=case.scale, block_table=dev.bt,
+                           token_seq=dev.ts, params=p)
+        else:
+            step()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # ---- dominant kernel: per-launch durations (events around each launch)
+    K2 = max(20, min(args.steps, 500))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K2)]
+    for a, b in evs:
+        a.record()
+        kernel_only()
+        b.record()
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    # ---- same kernel after evicting caches (1 GiB written between launches, not timed)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    cold = []
+    for _ in range(args.cold_launches):
+        flush.fill_(1.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        kernel_only()
+        b.record()
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    cold_ms = float(np.median(cold))
+    del flush
+
+    n_valid = algorithmic_counts(case)
+    row_bytes = 1152 if case.kv_format == "bf16" else 656
+    gathered = n_valid * row_bytes
+    flops = n_valid * h * 2 * (576 + 512)
+    tokens_per_s = T / (ms_per_step * 1e-3)
+    hbm_bound = h < 64
+    if hbm_bound:
+        achieved = gathered / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
+    else:
+        achieved = flops / (kern_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+    roof["kernel"] = "smla_fwd_bf16" + ("" if pl.num_splits == 1 else " (split partials)")
+    roof["kernel_us"] = round(kern_ms * 1e3, 2)
+    roof["algorithmic_bytes"] = gathered
+    roof["algorithmic_flops"] = flops
+
+    res = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl_name, "num_tokens": T, "num_heads": h, "topk": case.topk,
+                   "kv_format": case.kv_format, "page_size": case.page_size, "tiling": tiling,
+                   "num_splits": pl.num_splits, "kernel_variant": args.variant,
+                   "grid": pl.grid, "threads": pl.threads},
+        "gathered_GBps_per_step": round(gathered / (ms_per_step * 1e-3) / 1e9, 1),
+        "mfma_frac_per_step": round(flops / (ms_per_step * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 5),
+        "wall_s_timed": round(wall, 4),
+        "roofline": roof,
+        "cold_cache": {"kernel_us_median": round(cold_ms * 1e3, 2),
+                       "gathered_GBps": round(gathered / (cold_ms * 1e-3) / 1e9, 1),
+                       "hbm_frac": round(gathered / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                       "note": "1 GiB written between launches to evict L2 and MALL"},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

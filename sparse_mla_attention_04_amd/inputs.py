@@ -336,3 +336,21 @@ def make_mini(seed: int = 7, num_heads: int = 8, topk: int = 300, kv_format: str
     return build_case("mini", seed=seed, hist=[hist] * num_seqs, new=[tokens_per_seq] * num_seqs,
                       num_heads=num_heads, topk=topk, kv_format=kv_format, idx_stride=idx_stride,
                       drop_frac=drop_frac, page_size=page_size, query_positions=qpos)
+
+
+class DeviceCase:
+    """Device copies of a Case's arrays (torch tensors on `device`): q bf16
+    [T, H, 576], the cache (bf16 [pages, P, 576] or uint8 [pages, page_bytes]),
+    topk_idx int32, block_table int32, token_seq int32.  Upload only."""
+
+    def __init__(self, case: Case, device="cuda", idx: Optional[np.ndarray] = None):
+        import torch
+        self.case = case
+        self.q = torch.from_numpy(np.ascontiguousarray(case.q).view(np.int16)).to(device).view(torch.bfloat16)
+        if case.kv_format == "bf16":
+            self.kv = torch.from_numpy(case.kv.view(np.int16)).to(device).view(torch.bfloat16)
+        else:
+            self.kv = torch.from_numpy(case.kv).to(device)
+        self.idx = torch.from_numpy(np.ascontiguousarray(case.topk_idx if idx is None else idx)).to(device)
+        self.bt = torch.from_numpy(case.block_table).to(device)
+        self.ts = torch.from_numpy(case.token_seq).to(device)

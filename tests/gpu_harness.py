@@ -12,6 +12,7 @@ import torch
 
 from oracle import sparse_mla_oracle as O
 from sparse_mla_attention_04_amd import binding as B
+from sparse_mla_attention_04_amd import inputs as G
 
 OUT_ATOL = 1e-2
 OUT_RTOL = 1e-2
@@ -23,19 +24,7 @@ def say(*a):
     print(*a, flush=True)
 
 
-class Dev:
-    """Device copies of a Case (q, cache, indices, block table, token -> sequence)."""
-
-    def __init__(self, case, device="cuda", idx=None):
-        self.case = case
-        self.q = torch.from_numpy(np.ascontiguousarray(case.q).view(np.int16)).to(device).view(torch.bfloat16)
-        if case.kv_format == "bf16":
-            self.kv = torch.from_numpy(case.kv.view(np.int16)).to(device).view(torch.bfloat16)
-        else:
-            self.kv = torch.from_numpy(case.kv).to(device)
-        self.idx = torch.from_numpy(np.ascontiguousarray(case.topk_idx if idx is None else idx)).to(device)
-        self.bt = torch.from_numpy(case.block_table).to(device)
-        self.ts = torch.from_numpy(case.token_seq).to(device)
+Dev = G.DeviceCase
 
 
 def slot_indices(case, idx=None) -> np.ndarray:
