@@ -48,6 +48,7 @@ constexpr int ROW_BYTES = D_QK * 2;     // bf16 cache row
 constexpr int LIST_CAP = 2048;          // index entries compacted per pass
 constexpr float NEG_INF = -__builtin_inff();
 constexpr float LN2 = 0.69314718055994530942f;
+constexpr float REF_HEADROOM = 64.0f;   // p = 2^(x - ref) may reach 2^64 before a second pass is forced
 
 template <int HG_, int NRG_, int RT_, int NST_>
 struct Shape {
@@ -117,6 +118,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" : : : "
 
 __device__ __forceinline__ float wave_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
@@ -158,21 +160,6 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd_bf16(FwdArgs a) {
   const int hg = wave % S::HG, rg = wave / S::HG;
   const int g4 = lane >> 4, n = lane & 15;
 
-  // ---- queries of this wave's 16 heads, in the MFMA B-operand layout:
-  //      lane (g4, n) holds head hg*16+n, dims 32*kk + 8*g4 .. +7
-  bf16x8 qb[18];
-  {
-    const int head = hg * 16 + n;
-    if (head < a.h) {
-      const uint16_t* qp = a.q + (int64_t)t * a.q_st + (int64_t)head * a.q_sh + 8 * g4;
-#pragma unroll
-      for (int kk = 0; kk < 18; ++kk) qb[kk] = *reinterpret_cast<const bf16x8*>(qp + 32 * kk);
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < 18; ++kk) qb[kk] = bf16x8{};
-    }
-  }
-
   // ---- per-lane LDS offsets inside a tile
   // tile layout: position(r, c) = (c / 8) * RT * 8 + r * 8 + ((c % 8) ^ ((r >> 1) & 7)), 16 B each
   uint32_t kofs[S::NF][2];     // K operand: row 16f+n, chunk 4*kk+g4
@@ -194,7 +181,9 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd_bf16(FwdArgs a) {
   f32x4 o[32];
 #pragma unroll
   for (int f = 0; f < 32; ++f) o[f] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = NEG_INF, l_run = 0.f;
+  float m_run = NEG_INF, l_run = 0.f;   // exponent reference and row sum (per head lane)
+  float m_seen = NEG_INF;                 // true running maximum
+  bool overflow = false;
 
   // ---- index range of this split
   const int64_t c0 = (int64_t)a.topk * sp / S_;
@@ -208,20 +197,43 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd_bf16(FwdArgs a) {
     bt_row = seq_ok ? (int64_t)seq * a.bt_stride : 0;
   }
 
-  // make the compiler's wait for the query loads happen before any gather is in flight
+  // raw index entries of the first pass are requested before the queries so
+  // that their latencies overlap; thread tid owns entries cs + tid*EPT + i
+  int raw[S::EPT];
+  auto load_raw = [&](int64_t cs, int64_t ce) {
 #pragma unroll
-  for (int kk = 0; kk < 18; ++kk) asm volatile("" : : "v"(qb[kk]));
+    for (int i = 0; i < S::EPT; ++i) {
+      const int64_t e = cs + (int64_t)tid * S::EPT + i;
+      raw[i] = (e < ce) ? idx_row[e] : -1;
+    }
+  };
+  load_raw(c0, (c0 + LIST_CAP < c1) ? c0 + LIST_CAP : c1);
 
+  // ---- queries of this wave's 16 heads, in the MFMA B-operand layout:
+  //      lane (g4, n) holds head hg*16+n, dims 32*kk + 8*g4 .. +7
+  bf16x8 qb[18];
+  {
+    const int head = hg * 16 + n;
+    if (head < a.h) {
+      const uint16_t* qp = a.q + (int64_t)t * a.q_st + (int64_t)head * a.q_sh + 8 * g4;
+#pragma unroll
+      for (int kk = 0; kk < 18; ++kk) qb[kk] = *reinterpret_cast<const bf16x8*>(qp + 32 * kk);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 18; ++kk) qb[kk] = bf16x8{};
+    }
+  }
+
+  for (int pass = 0; pass < 2; ++pass) {
   for (int64_t cs = c0; cs < c1; cs += LIST_CAP) {
     const int64_t ce = (cs + LIST_CAP < c1) ? cs + LIST_CAP : c1;
-    // ---- compaction: thread tid owns entries cs + tid*EPT .. +EPT-1 (order preserved)
+    if (cs != c0 || pass != 0) load_raw(cs, ce);
+    // ---- compaction (order preserved)
     int sl[S::EPT];
     int cnt = 0;
 #pragma unroll
     for (int i = 0; i < S::EPT; ++i) {
-      const int64_t e = cs + (int64_t)tid * S::EPT + i;
-      int s = -1;
-      if (e < ce) s = translate(a, idx_row[e], seq_ok, bt_row);
+      const int s = translate(a, raw[i], seq_ok, bt_row);
       sl[i] = s;
       cnt += (s >= 0);
     }
@@ -288,13 +300,18 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd_bf16(FwdArgs a) {
       f32x4 sc[S::NF];
 #pragma unroll
       for (int f = 0; f < S::NF; ++f) {
+        // all 18 K operands of the fragment are requested before its first
+        // MFMA, so the LDS latency is paid once per fragment
+        bf16x8 kb[18];
+#pragma unroll
+        for (int kk = 0; kk < 18; ++kk)
+          kb[kk] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[f][kk & 1] + (kk >> 1) * S::RT * 128);
+        __builtin_amdgcn_sched_barrier(0);
         f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
 #pragma unroll
         for (int kk = 0; kk < 18; kk += 2) {
-          const bf16x8 k0 = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[f][0] + (kk >> 1) * S::RT * 128);
-          const bf16x8 k1 = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[f][1] + (kk >> 1) * S::RT * 128);
-          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[kk], acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[kk + 1], acc1, 0, 0, 0);
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qb[kk], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk + 1], qb[kk + 1], acc1, 0, 0, 0);
         }
         sc[f] = acc0 + acc1;
       }
@@ -313,31 +330,48 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd_bf16(FwdArgs a) {
         }
       mx = fmaxf(mx, wave_xor(mx, 16));
       mx = fmaxf(mx, wave_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
+      // Fixed exponent reference: the first tile's max becomes the row's
+      // reference and later tiles use it unchanged (p <= 2^REF_HEADROOM), so
+      // the accumulators never need rescaling.  A tile that exceeds the
+      // reference by more than the headroom flags the work-group, which then
+      // recomputes the row once with its true maximum as the reference.
+      m_seen = fmaxf(m_seen, mx);
+      if (m_run == NEG_INF) m_run = mx;
+      overflow |= (mx > m_run + REF_HEADROOM);
       float psum = 0.f;
       float pv[S::NF][4];
 #pragma unroll
       for (int f = 0; f < S::NF; ++f)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          pv[f][j] = fast_exp2(x[f][j] - m_new);
+          pv[f][j] = fast_exp2(x[f][j] - m_run);
           psum += pv[f][j];
         }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int f = 0; f < 32; ++f) o[f] *= alpha;
+      l_run += psum;
       // P.V
+      // V^T operands are read in groups of 8 output fragments, the next
+      // group's transposing reads in flight while the current group's MFMAs run
       if constexpr (S::RT == 16) {
         bf16x4 pb;
 #pragma unroll
         for (int j = 0; j < 4; ++j) pb[j] = (__bf16)pv[0][j];
+        bf16x4 va[2][8];
+        auto load_grp = [&](int g, int buf) {
 #pragma unroll
-        for (int f = 0; f < 32; ++f) {
-          const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (LDS_AS bf16x4*)(tp + vofs[0][f & 3] + (f >> 2) * S::RT * 128));
-          o[f] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[f], 0, 0, 0);
+          for (int i = 0; i < 8; ++i) {
+            const int f = 8 * g + i;
+            va[buf][i] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (LDS_AS bf16x4*)(tp + vofs[0][f & 3] + (f >> 2) * S::RT * 128));
+          }
+        };
+        load_grp(0, 0);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          if (g + 1 < 4) load_grp(g + 1, (g + 1) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            o[8 * g + i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[g & 1][i], pb, o[8 * g + i], 0, 0, 0);
         }
       } else {
         bf16x8 pb;
@@ -346,17 +380,33 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd_bf16(FwdArgs a) {
           pb[j] = (__bf16)pv[0][j];
           pb[4 + j] = (__bf16)pv[1][j];
         }
+        bf16x8 va[2][8];
+        auto load_grp = [&](int g, int buf) {
 #pragma unroll
-        for (int f = 0; f < 32; ++f) {
-          const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (LDS_AS bf16x4*)(tp + vofs[0][f & 3] + (f >> 2) * S::RT * 128));
-          const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (LDS_AS bf16x4*)(tp + vofs[1][f & 3] + (f >> 2) * S::RT * 128));
-          const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[f], 0, 0, 0);
+          for (int i = 0; i < 8; ++i) {
+            const int f = 8 * g + i;
+            const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (LDS_AS bf16x4*)(tp + vofs[0][f & 3] + (f >> 2) * S::RT * 128));
+            const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (LDS_AS bf16x4*)(tp + vofs[1][f & 3] + (f >> 2) * S::RT * 128));
+            va[buf][i] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
+        };
+        load_grp(0, 0);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          if (g + 1 < 4) load_grp(g + 1, (g + 1) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            o[8 * g + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[g & 1][i], pb, o[8 * g + i], 0, 0, 0);
         }
       }
     };
+
+    // the compiler's wait for the query loads lands here, before any gather is in flight
+#pragma unroll
+    for (int kk = 0; kk < 18; ++kk) asm volatile("" : : "v"(qb[kk]));
 
     // ---- the pipeline
     int iss = 0;
@@ -387,6 +437,15 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd_bf16(FwdArgs a) {
     }
     wait_vm<0>();
     __syncthreads();   // the list is rewritten by the next pass
+  }
+  // rare: some tile exceeded the reference headroom -> recompute the row
+  // (every wave of the work-group takes the same decision)
+  if (!__syncthreads_or(overflow ? 1 : 0)) break;
+  m_run = m_seen;
+  l_run = 0.f;
+  overflow = false;
+#pragma unroll
+  for (int f = 0; f < 32; ++f) o[f] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   // ---- epilogue: merge the row groups of each head group, normalise, write
@@ -456,40 +515,72 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd_bf16(FwdArgs a) {
 }
 
 // Merge the KV splits of each query row by their lse, in split order.
+// Thread = (row, head, 8 output dims); SMAX > 0 unrolls the split loop so the
+// loads of all splits are in flight together (SMAX = 0: any split count).
+template <int SMAX>
 __global__ void __launch_bounds__(256) smla_lse_combine(CombineArgs a) {
   const int t = blockIdx.x;
+  const int item = blockIdx.y * 256 + threadIdx.x;
+  if (item >= a.h * 64) return;
+  const int head = item >> 6, c = item & 63;
   const int S_ = a.num_splits;
-  for (int item = threadIdx.x; item < a.h * 64; item += 256) {
-    const int head = item >> 6, c = item & 63;
-    float M = NEG_INF;
-    for (int s = 0; s < S_; ++s) M = fmaxf(M, a.ws_lse[((int64_t)t * S_ + s) * a.h + head]);
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float L = 0.f;
-    if (M != NEG_INF) {
-      for (int s = 0; s < S_; ++s) {
-        const int64_t u = (int64_t)t * S_ + s;
-        const float ls = a.ws_lse[u * a.h + head];
-        const float w = fast_exp2((ls - M) * 1.44269504088896340736f);
-        L += w;
-        const f32x4* src = reinterpret_cast<const f32x4*>(a.ws_out + (u * a.h + head) * D_V + 8 * c);
-        const f32x4 v0 = src[0], v1 = src[1];
+  const int64_t u0 = (int64_t)t * S_;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float M = NEG_INF, L = 0.f;
+  if constexpr (SMAX > 0) {
+    float ls[SMAX];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[j] += w * v0[j];
-          acc[4 + j] += w * v1[j];
+    for (int s = 0; s < SMAX; ++s) ls[s] = (s < S_) ? a.ws_lse[(u0 + s) * a.h + head] : NEG_INF;
+    f32x4 v0[SMAX], v1[SMAX];
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) {
+      if (s < S_) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(a.ws_out + ((u0 + s) * a.h + head) * D_V + 8 * c);
+        v0[s] = src[0];
+        v1[s] = src[1];
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) M = fmaxf(M, ls[s]);
+    if (M != NEG_INF) {
+#pragma unroll
+      for (int s = 0; s < SMAX; ++s) {
+        if (s < S_) {
+          const float w = fast_exp2((ls[s] - M) * 1.44269504088896340736f);
+          L += w;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[j] += w * v0[s][j];
+            acc[4 + j] += w * v1[s][j];
+          }
         }
       }
     }
-    const bool empty = !(L > 0.f);
-    const float inv = empty ? 0.f : 1.f / L;
-    u32x4 pk;
+  } else {
+    for (int s = 0; s < S_; ++s) M = fmaxf(M, a.ws_lse[(u0 + s) * a.h + head]);
+    if (M != NEG_INF) {
+      for (int s = 0; s < S_; ++s) {
+        const int64_t u = u0 + s;
+        const float w = fast_exp2((a.ws_lse[u * a.h + head] - M) * 1.44269504088896340736f);
+        L += w;
+        const f32x4* src = reinterpret_cast<const f32x4*>(a.ws_out + (u * a.h + head) * D_V + 8 * c);
+        const f32x4 x0 = src[0], x1 = src[1];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      pk[j] = (uint32_t)f32_to_bf16_bits(acc[2 * j] * inv) |
-              ((uint32_t)f32_to_bf16_bits(acc[2 * j + 1] * inv) << 16);
-    *reinterpret_cast<u32x4*>(a.out + (int64_t)t * a.out_st + (int64_t)head * a.out_sh + 8 * c) = pk;
-    if (c == 0) a.lse[(int64_t)t * a.lse_st + head] = empty ? NEG_INF : M + __logf(L);
+        for (int j = 0; j < 4; ++j) {
+          acc[j] += w * x0[j];
+          acc[4 + j] += w * x1[j];
+        }
+      }
+    }
   }
+  const bool empty = !(L > 0.f);
+  const float inv = empty ? 0.f : 1.f / L;
+  u32x4 pk;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    pk[j] = (uint32_t)f32_to_bf16_bits(acc[2 * j] * inv) | ((uint32_t)f32_to_bf16_bits(acc[2 * j + 1] * inv) << 16);
+  *reinterpret_cast<u32x4*>(a.out + (int64_t)t * a.out_st + (int64_t)head * a.out_sh + 8 * c) = pk;
+  if (c == 0) a.lse[(int64_t)t * a.lse_st + head] = empty ? NEG_INF : M + __logf(L);
 }
 
 // Kernel variants: (head groups, row groups, tile rows, stages).
@@ -534,7 +625,11 @@ hipError_t launch_fwd(const FwdArgs& a, int kv_format, int head_groups, int vari
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(smla_lse_combine, dim3((unsigned)a.T), dim3(256), 0, stream, a);
+  const dim3 grid((unsigned)a.T, (unsigned)((a.h * 64 + 255) / 256));
+  if (a.num_splits <= 4) hipLaunchKernelGGL(smla_lse_combine<4>, grid, dim3(256), 0, stream, a);
+  else if (a.num_splits <= 8) hipLaunchKernelGGL(smla_lse_combine<8>, grid, dim3(256), 0, stream, a);
+  else if (a.num_splits <= 16) hipLaunchKernelGGL(smla_lse_combine<16>, grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(smla_lse_combine<0>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -121,6 +121,30 @@ def test_repeated_index_returns_row_exactly(k):
     check(out, lse, ro, rl, "repeated index")
 
 
+@pytest.mark.parametrize("splits", [1, 3])
+def test_large_score_spread_recomputes_exactly(splits):
+    """A row whose later entries score far above its first tile (beyond the
+    kernel's exponent headroom) forces the one-time recomputation with the
+    exact maximum; the result must still match the oracle."""
+    say("large score spread", splits)
+    c = G.make_mini(seed=41, num_heads=16, topk=300, drop_frac=0.0)
+    kv = c.kv.copy()
+    flat = kv.reshape(-1, 576)
+    hot = 5                                           # physical row made to align with every query
+    qsign = np.sign((c.q[0, 0].astype(np.uint32) << 16).view(np.float32))
+    big = G.to_bf16_bits((16.0 * qsign).astype(np.float32))
+    flat[hot] = big
+    c2 = G.Case(**{**c.__dict__, "kv": kv})
+    from tests.gpu_harness import slot_indices
+    sidx = slot_indices(c2)
+    sidx[:, -1] = hot                                 # last entry of every row: the hot row
+    dev = Dev(c2, idx=sidx)
+    out, lse = to_np(*run_gpu(dev, logical=False, num_splits=splits))
+    from oracle import sparse_mla_oracle as O
+    ro, rl = O.sparse_mla_forward(c2.q, c2.kv, sidx, topk=c2.topk, scale=c2.scale, index_mode="slot")
+    check(out, lse, ro, rl, "score spread")
+
+
 def test_empty_and_out_of_range_rows():
     say("empty rows")
     c = G.make_mini(seed=28, num_heads=8, topk=100)
