@@ -55,7 +55,6 @@ int check_params(const smla_params* p) {
         return SMLA_ERR_INVALID_ARG;
     }
   }
-  if (p->kv_format == SMLA_KV_FP8_E4M3) return SMLA_ERR_UNSUPPORTED;   // fp8 kernel not built yet
   return SMLA_OK;
 }
 

@@ -45,24 +45,29 @@ typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 constexpr int D_QK = 576;
 constexpr int D_V = 512;
 constexpr int ROW_BYTES = D_QK * 2;     // bf16 cache row
+constexpr int FP8_ROW_BYTES = 640;      // fp8 cache row: 512 code bytes + 64 bf16 rope
+constexpr int FP8_SLOT_BYTES = 656;     // per-row share of an fp8 page (row + four fp32 scales)
 constexpr int LIST_CAP = 2048;          // index entries compacted per pass
 constexpr float NEG_INF = -__builtin_inff();
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float REF_HEADROOM = 64.0f;   // p = 2^(x - ref) may reach 2^64 before a second pass is forced
 
-template <int HG_, int NRG_, int RT_, int NST_>
+template <int HG_, int NRG_, int RT_, int NST_, int FMT_>
 struct Shape {
   static constexpr int HG = HG_;            // 16-head groups (waves per row group)
   static constexpr int NRG = NRG_;          // row groups (independent KV row streams)
   static constexpr int RT = RT_;            // rows per tile
   static constexpr int NST = NST_;          // tiles in flight per row group
+  static constexpr bool FP8 = FMT_ == 1;    // fp8 latent + bf16 rope rows, per-128-dim scales
   static constexpr int NW = HG * NRG;       // waves
   static constexpr int NTHR = NW * 64;
   static constexpr int NF = RT / 16;        // 16-row score fragments per tile
   static constexpr int NRH = RT / 8;        // 8-row DMA groups per tile
   static constexpr int RH_PER_WAVE = NRH / HG;
-  static constexpr int PER = 9 * RH_PER_WAVE;   // DMA instructions per wave per tile
-  static constexpr int TILE_BYTES = RT * ROW_BYTES;
+  static constexpr int NLINES = FP8 ? FP8_ROW_BYTES / 128 : ROW_BYTES / 128;   // 128-B lines per row
+  static constexpr int BODY_BYTES = RT * NLINES * 128;
+  static constexpr int TILE_BYTES = BODY_BYTES + (FP8 ? RT * 16 : 0);       // + fp32 block scales
+  static constexpr int PER = NLINES * RH_PER_WAVE + (FP8 ? 1 : 0);  // DMA instructions per wave per tile
   static constexpr int RING_BYTES = NRG * NST * TILE_BYTES;
   static constexpr int LIST_OFF = RING_BYTES;
   static constexpr int CNT_OFF = LIST_OFF + LIST_CAP * 4;
@@ -71,6 +76,7 @@ struct Shape {
   static constexpr int EPT = LIST_CAP / NTHR;   // index entries per thread per pass
   static constexpr bool SYNC = HG > 1;          // waves share tiles -> barrier per tile
   static_assert(RT == 16 || RT == 32, "tile rows");
+  static_assert(!FP8 || RT == 32, "the fp8 P.V step pairs two 16-row fragments");
   static_assert(NRH % HG == 0, "DMA groups must split evenly over the waves of a row group");
   static_assert((NST - 1) * PER <= 63, "vmcnt holds at most 63 outstanding loads");
   static_assert(NW * 32 * 64 * 16 <= RING_BYTES, "epilogue staging must fit in the ring");
@@ -126,6 +132,29 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, b);
 }
 
+// Byte offset of a cache row: bf16 rows are contiguous; fp8 pages hold the
+// page's rows first ([512 codes | 64 bf16 rope] each) and then their scales.
+template <bool FP8>
+__device__ __forceinline__ int64_t row_offset(const FwdArgs& a, int slot) {
+  if constexpr (FP8) {
+    const int64_t page = slot >> a.page_shift;
+    const int64_t rin = slot & ((1 << a.page_shift) - 1);
+    return page * ((int64_t)FP8_SLOT_BYTES << a.page_shift) + rin * FP8_ROW_BYTES;
+  } else {
+    return (int64_t)slot * ROW_BYTES;
+  }
+}
+
+// 8 fp8 E4M3 codes (two 32-bit words) -> 8 bf16 values, exact.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+  const bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, false);
+  const bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, true);
+  const bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, false);
+  const bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, true);
+  return bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+}
+
 // Translate one index entry to a physical cache row; -1 when skipped.
 __device__ __forceinline__ int translate(const FwdArgs& a, int j, int seq_ok, int64_t bt_row) {
   if (j < 0) return -1;
@@ -139,7 +168,7 @@ __device__ __forceinline__ int translate(const FwdArgs& a, int j, int seq_ok, in
 }
 
 template <class S>
-__global__ void __launch_bounds__(S::NTHR, 1) smla_fwd_bf16(FwdArgs a) {
+__global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S::LDS_BYTES];
   int* list = reinterpret_cast<int*>(smem + S::LIST_OFF);
   int* wcnt = reinterpret_cast<int*>(smem + S::CNT_OFF);
@@ -176,6 +205,25 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd_bf16(FwdArgs a) {
 #pragma unroll
     for (int p = 0; p < 4; ++p)
       vofs[f][p] = (uint32_t)(rv * 8 + ((2 * p + (cq >> 1)) ^ swv)) * 16u + (uint32_t)(cq & 1) * 8u;
+  }
+
+  // fp8 rows: 40 chunks of 16 B ([512 codes | 64 bf16 rope]) laid out like the bf16 tile
+  uint32_t k8ofs[S::FP8 ? S::NF : 1][4];   // latent codes: row 16f+n, 8 B at dims 32*kk + 8*g4
+  uint32_t tr8ofs[S::FP8 ? 8 : 1];         // transposing fp8 read: row kmap(g4, n>>1), 8 B at dims 16f + 8*(n&1)
+  if constexpr (S::FP8) {
+#pragma unroll
+    for (int f = 0; f < S::NF; ++f) {
+      const int r = 16 * f + n;
+      const int sw = (r >> 1) & 7;
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        k8ofs[f][p] = (uint32_t)(r * 8 + ((2 * p + (g4 >> 1)) ^ sw)) * 16u + (uint32_t)(g4 & 1) * 8u;
+    }
+    const int kq = n >> 1;
+    const int rr = (kq < 4) ? 4 * g4 + kq : 16 + 4 * g4 + (kq - 4);
+    const int swr = (rr >> 1) & 7;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) tr8ofs[p] = (uint32_t)(rr * 8 + (p ^ swr)) * 16u + (uint32_t)(n & 1) * 8u;
   }
 
   f32x4 o[32];
@@ -278,7 +326,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd_bf16(FwdArgs a) {
         li = (li < n_valid) ? li : n_valid - 1;           // tail rows repeat the last valid row
         const int slot = list[li];
         const int q = (lane & 7) ^ ((r >> 1) & 7);
-        const uint8_t* g = a.kv + (int64_t)slot * ROW_BYTES + q * 16;
+        const uint8_t* g = a.kv + row_offset<S::FP8>(a, slot) + q * 16;
         const uint32_t mb = tl + (uint32_t)rh * 1024u;
         // line L of the row lands at tile position L*RT*8 + rh*64 + lane
         dma16<0 * 128>(g, mb + 0 * (S::RT * 128 - 128));
@@ -286,10 +334,27 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd_bf16(FwdArgs a) {
         dma16<2 * 128>(g, mb + 2 * (S::RT * 128 - 128));
         dma16<3 * 128>(g, mb + 3 * (S::RT * 128 - 128));
         dma16<4 * 128>(g, mb + 4 * (S::RT * 128 - 128));
-        dma16<5 * 128>(g, mb + 5 * (S::RT * 128 - 128));
-        dma16<6 * 128>(g, mb + 6 * (S::RT * 128 - 128));
-        dma16<7 * 128>(g, mb + 7 * (S::RT * 128 - 128));
-        dma16<8 * 128>(g, mb + 8 * (S::RT * 128 - 128));
+        if constexpr (!S::FP8) {
+          dma16<5 * 128>(g, mb + 5 * (S::RT * 128 - 128));
+          dma16<6 * 128>(g, mb + 6 * (S::RT * 128 - 128));
+          dma16<7 * 128>(g, mb + 7 * (S::RT * 128 - 128));
+          dma16<8 * 128>(g, mb + 8 * (S::RT * 128 - 128));
+        }
+      }
+      if constexpr (S::FP8) {
+        // the block scales of this wave's share of the tile rows, 16 B per row
+        constexpr int SR = S::RT / S::HG;
+        if (lane < SR) {
+          const int r = hg * SR + lane;
+          int li = tstart + r;
+          li = (li < n_valid) ? li : n_valid - 1;
+          const int slot = list[li];
+          const int64_t page = slot >> a.page_shift;
+          const int64_t rin = slot & ((1 << a.page_shift) - 1);
+          const uint8_t* g = a.kv + page * ((int64_t)FP8_SLOT_BYTES << a.page_shift) +
+                             ((int64_t)FP8_ROW_BYTES << a.page_shift) + rin * 16;
+          dma16<0>(g, tl + S::BODY_BYTES + (uint32_t)(hg * SR * 16));
+        }
       }
     };
     auto compute = [&](int it) {
@@ -298,6 +363,43 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd_bf16(FwdArgs a) {
       const LDS_AS uint8_t* tp = lds + toff;
       // scores S^T[row][head] for this wave's 16 heads
       f32x4 sc[S::NF];
+      f32x4 sv[S::FP8 ? S::NF : 1][4];   // fp8: block scales of the lane's accumulator rows 16f+4*g4+j
+      if constexpr (S::FP8) {
+#pragma unroll
+        for (int f = 0; f < S::NF; ++f)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            sv[f][j] = *reinterpret_cast<const LDS_AS f32x4*>(tp + S::BODY_BYTES + (16 * f + 4 * g4 + j) * 16);
+#pragma unroll
+        for (int f = 0; f < S::NF; ++f) {
+          // latent: 16 k-steps of 8 fp8 codes per lane, dequantised exactly to
+          // bf16; each 128-dim block accumulates separately and is scaled in fp32
+          typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+          u32x2 kw[16];
+#pragma unroll
+          for (int kk = 0; kk < 16; ++kk)
+            kw[kk] = *reinterpret_cast<const LDS_AS u32x2*>(tp + k8ofs[f][kk & 3] + (kk >> 2) * S::RT * 128);
+          bf16x8 kr[2];
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
+            kr[kk] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[f][kk] + 4 * S::RT * 128);
+          __builtin_amdgcn_sched_barrier(0);
+          f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int blk = 0; blk < 4; ++blk) {
+            f32x4 ab = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 4 * blk; kk < 4 * blk + 4; ++kk)
+              ab = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(kw[kk][0], kw[kk][1]), qb[kk], ab, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] += ab[j] * sv[f][j][blk];
+          }
+          f32x4 ar = f32x4{0.f, 0.f, 0.f, 0.f};
+          ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[0], qb[16], ar, 0, 0, 0);
+          ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[1], qb[17], ar, 0, 0, 0);
+          sc[f] = acc + ar;
+        }
+      } else
 #pragma unroll
       for (int f = 0; f < S::NF; ++f) {
         // all 18 K operands of the fragment are requested before its first
@@ -351,7 +453,37 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd_bf16(FwdArgs a) {
       // P.V
       // V^T operands are read in groups of 8 output fragments, the next
       // group's transposing reads in flight while the current group's MFMAs run
-      if constexpr (S::RT == 16) {
+      if constexpr (S::FP8) {
+        // P' = P * scale(row, block): one bf16 operand per 128-dim block, the
+        // 8 k-slots of a lane being rows 4*g4+j (fragment 0) and 16+4*g4+j (fragment 1)
+        bf16x8 pb[4];
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            pb[blk][j] = (__bf16)(pv[0][j] * sv[0][j][blk]);
+            pb[blk][4 + j] = (__bf16)(pv[1][j] * sv[1][j][blk]);
+          }
+        typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+        i32x2 vw[2][8];
+        auto load_grp = [&](int g, int buf) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int f = 8 * g + i;
+            vw[buf][i] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2*)(tp + tr8ofs[f & 7] + (f >> 3) * S::RT * 128));
+          }
+        };
+        load_grp(0, 0);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          if (g + 1 < 4) load_grp(g + 1, (g + 1) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            o[8 * g + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                fp8x8_to_bf16((uint32_t)vw[g & 1][i][0], (uint32_t)vw[g & 1][i][1]), pb[g], o[8 * g + i], 0, 0, 0);
+        }
+      } else if constexpr (S::RT == 16) {
         bf16x4 pb;
 #pragma unroll
         for (int j = 0; j < 4; ++j) pb[j] = (__bf16)pv[0][j];
@@ -583,12 +715,15 @@ __global__ void __launch_bounds__(256) smla_lse_combine(CombineArgs a) {
   if (c == 0) a.lse[(int64_t)t * a.lse_st + head] = empty ? NEG_INF : M + __logf(L);
 }
 
-// Kernel variants: (head groups, row groups, tile rows, stages).
-using V_H1_A = Shape<1, 4, 16, 2>;
-using V_H1_B = Shape<1, 2, 16, 4>;
-using V_H2_A = Shape<2, 2, 32, 2>;
-using V_H2_B = Shape<2, 1, 32, 4>;
-using V_H4_A = Shape<4, 1, 32, 4>;
+// Kernel variants: (head groups, row groups, tile rows, stages, format).
+using V_H1_A = Shape<1, 4, 16, 2, 0>;
+using V_H1_B = Shape<1, 2, 16, 4, 0>;
+using V_H2_A = Shape<2, 2, 32, 2, 0>;
+using V_H2_B = Shape<2, 1, 32, 4, 0>;
+using V_H4_A = Shape<4, 1, 32, 4, 0>;
+using F_H1_A = Shape<1, 2, 32, 3, 1>;
+using F_H2_A = Shape<2, 1, 32, 4, 1>;
+using F_H4_A = Shape<4, 1, 32, 7, 1>;
 
 template <class S>
 FwdShape shape_of() {
@@ -597,14 +732,22 @@ FwdShape shape_of() {
 
 template <class S>
 hipError_t launch_one(const FwdArgs& a, int64_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL(smla_fwd_bf16<S>, dim3((unsigned)grid), dim3(S::NTHR), 0, stream, a);
+  hipLaunchKernelGGL(smla_fwd<S>, dim3((unsigned)grid), dim3(S::NTHR), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool fwd_shape(int kv_format, int head_groups, int variant, FwdShape* shape) {
-  if (kv_format != 0) return false;
+  if (kv_format == 1) {
+    if (variant != 0) return false;
+    switch (head_groups) {
+      case 1: *shape = shape_of<F_H1_A>(); return true;
+      case 2: *shape = shape_of<F_H2_A>(); return true;
+      case 4: *shape = shape_of<F_H4_A>(); return true;
+      default: return false;
+    }
+  }
   switch (head_groups) {
     case 1: *shape = variant == 1 ? shape_of<V_H1_B>() : shape_of<V_H1_A>(); return variant <= 1;
     case 2: *shape = variant == 1 ? shape_of<V_H2_B>() : shape_of<V_H2_A>(); return variant <= 1;
@@ -615,7 +758,14 @@ bool fwd_shape(int kv_format, int head_groups, int variant, FwdShape* shape) {
 
 hipError_t launch_fwd(const FwdArgs& a, int kv_format, int head_groups, int variant, int64_t grid,
                       hipStream_t stream) {
-  if (kv_format != 0) return hipErrorInvalidValue;
+  if (kv_format == 1) {
+    switch (head_groups) {
+      case 1: return launch_one<F_H1_A>(a, grid, stream);
+      case 2: return launch_one<F_H2_A>(a, grid, stream);
+      case 4: return launch_one<F_H4_A>(a, grid, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (head_groups) {
     case 1: return variant == 1 ? launch_one<V_H1_B>(a, grid, stream) : launch_one<V_H1_A>(a, grid, stream);
     case 2: return variant == 1 ? launch_one<V_H2_B>(a, grid, stream) : launch_one<V_H2_A>(a, grid, stream);

@@ -316,3 +316,41 @@ def test_many_tokens_grid():
     out, lse = to_np(*run_gpu(dev))
     rows = _sample_rows(c, 64, seed=5)
     check(out[rows], lse[rows], *oracle(c, rows=rows), what="T=65536")
+
+
+# --------------------------------------------------------------------------- fp8 latent cache
+
+@pytest.mark.parametrize("h", [8, 16, 32, 64])
+def test_fp8_mini_heads(h):
+    say("fp8 mini heads", h)
+    c = G.make_mini(seed=51, num_heads=h, topk=300, kv_format="fp8")
+    out, lse = to_np(*run_gpu(Dev(c)))
+    check(out, lse, *oracle(c), what="fp8 mini h=%d" % h)
+
+
+@pytest.mark.parametrize("splits", [1, 3, 8])
+def test_fp8_splits_and_slot_mode(splits):
+    say("fp8 splits", splits)
+    c = G.make_mini(seed=52, num_heads=8, topk=333, kv_format="fp8", drop_frac=0.2)
+    dev = Dev(c)
+    out, lse = to_np(*run_gpu(dev, num_splits=splits))
+    check(out, lse, *oracle(c), what="fp8 split %d" % splits)
+    sidx = torch.from_numpy(slot_indices(c)).cuda()
+    os_, ls = to_np(*run_gpu(dev, logical=False, idx_t=sidx, num_splits=splits))
+    assert np.array_equal(out, os_) and np.array_equal(lse, ls)
+
+
+def test_fp8_page_size_16_and_wide_index():
+    say("fp8 P=16 wide idx")
+    c = G.make_mini(seed=53, num_heads=16, topk=256, kv_format="fp8", page_size=16, idx_stride=259)
+    out, lse = to_np(*run_gpu(Dev(c)))
+    check(out, lse, *oracle(c), what="fp8 P=16")
+
+
+def test_c5_fp8_sampled():
+    say("c5 fp8")
+    c = G.make_config("c5_fp8")
+    dev = Dev(c)
+    out, lse = to_np(*run_gpu(dev))
+    rows = _sample_rows(c, 48, seed=5)
+    check(out[rows], lse[rows], *oracle(c, rows=rows), what="c5")
