@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--cold-launches", type=int, default=50)
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (calibrates HBM byte counters)")
     return ap.parse_args()
 
 
@@ -75,6 +77,27 @@ def algorithmic_counts(case):
     page = case.block_table[case.token_seq[:, None], np.minimum(blk, case.block_table.shape[1] - 1)]
     valid &= (page >= 0) & (page < case.num_pages)
     return int(valid.sum())
+
+
+def counted_traffic(workload_name):
+    """HBM bytes per launch of the attention kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE runs (copy-calibrated), or None when no
+    counters exist for this workload or the kernel source changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_%s.json" % workload_name)
+    src = os.path.join(ROOT, "sparse_mla_attention_04_amd", "csrc", "smla_fwd.hip")
+    if not os.path.exists(path):
+        return None, None
+    with open(path) as f:
+        rec = json.load(f)
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec.get("kernel_source_sha256"):
+            return None, "stale: kernel source changed since %s" % rec.get("commit")
+    for name, v in rec["kernels"].items():
+        if "smla_fwd<" in name:
+            return v["fetch_bytes"] + v["write_bytes"], "fetch %.0f + write %.0f B (copy-calibrated, %s)" % (
+                v["fetch_bytes"], v["write_bytes"], os.path.basename(path))
+    return None, None
 
 
 def cpu_baseline(case, seconds):
@@ -109,6 +132,14 @@ def main():
               "MI355X (no collectives); --gpus %d is not supported." % args.gpus, flush=True)
         sys.exit(2)
     import torch
+    if args.copy_reference:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_reference_bytes_read": src.numel() * 4, "launches": 5}), flush=True)
+        return
     from sparse_mla_attention_04_amd import binding as B
     from sparse_mla_attention_04_amd.inputs import DeviceCase as Dev
 
@@ -191,7 +222,10 @@ def main():
         achieved = flops / (kern_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
-    roof["kernel"] = "smla_fwd_bf16" + ("" if pl.num_splits == 1 else " (split partials)")
+    traffic, traffic_note = counted_traffic(args.workload)
+    roof["traffic"] = None if traffic is None else round(traffic)
+    roof["traffic_note"] = traffic_note
+    roof["kernel"] = "smla_fwd" + ("" if pl.num_splits == 1 else " (split partials)")
     roof["kernel_us"] = round(kern_ms * 1e3, 2)
     roof["algorithmic_bytes"] = gathered
     roof["algorithmic_flops"] = flops

@@ -237,13 +237,6 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
   const int64_t c0 = (int64_t)a.topk * sp / S_;
   const int64_t c1 = (int64_t)a.topk * (sp + 1) / S_;
   const int32_t* idx_row = a.topk_idx + (int64_t)t * a.idx_stride;
-  int seq = 0, seq_ok = 1;
-  int64_t bt_row = 0;
-  if (a.index_mode == 1) {
-    seq = a.token_seq[t];
-    seq_ok = (seq >= 0 && seq < a.num_seqs);
-    bt_row = seq_ok ? (int64_t)seq * a.bt_stride : 0;
-  }
 
   // raw index entries of the first pass are requested before the queries so
   // that their latencies overlap; thread tid owns entries cs + tid*EPT + i
@@ -270,6 +263,16 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
 #pragma unroll
       for (int kk = 0; kk < 18; ++kk) qb[kk] = bf16x8{};
     }
+  }
+
+  // the row's sequence (LOGICAL mode) is requested after the index entries and
+  // queries so its latency overlaps theirs
+  int seq_ok = 1;
+  int64_t bt_row = 0;
+  if (a.index_mode == 1) {
+    const int seq = a.token_seq[t];
+    seq_ok = (seq >= 0 && seq < a.num_seqs);
+    bt_row = seq_ok ? (int64_t)seq * a.bt_stride : 0;
   }
 
   for (int pass = 0; pass < 2; ++pass) {
