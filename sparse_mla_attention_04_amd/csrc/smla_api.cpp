@@ -24,7 +24,14 @@ int log2i(int64_t v) {
   return s;
 }
 
-// Parameter checks that need no pointers.
+int head_groups_for(const smla_params* p) {
+  if (p->tiling == SMLA_TILING_PAD64) return 4;
+  if (p->num_heads <= 16) return 1;
+  if (p->num_heads <= 32) return 2;
+  return 4;
+}
+
+// Parameter checks that need no pointers (and no device).
 int check_params(const smla_params* p) {
   if (!p) return SMLA_ERR_INVALID_ARG;
   if (p->kernel_variant < 0) return SMLA_ERR_INVALID_ARG;
@@ -37,6 +44,12 @@ int check_params(const smla_params* p) {
   if (p->index_mode != SMLA_IDX_SLOT && p->index_mode != SMLA_IDX_LOGICAL) return SMLA_ERR_INVALID_ARG;
   if (p->tiling < SMLA_TILING_AUTO || p->tiling > SMLA_TILING_PAD64) return SMLA_ERR_INVALID_ARG;
   if (p->num_splits < 0) return SMLA_ERR_INVALID_ARG;
+  if (p->num_heads >= 1 && p->num_heads <= SMLA_MAX_HEADS &&
+      (p->kv_format == SMLA_KV_BF16 || p->kv_format == SMLA_KV_FP8_E4M3) &&
+      p->tiling >= SMLA_TILING_AUTO && p->tiling <= SMLA_TILING_PAD64) {
+    smla::FwdShape sh{};
+    if (!smla::fwd_shape(p->kv_format, head_groups_for(p), p->kernel_variant, &sh)) return SMLA_ERR_UNSUPPORTED;
+  }
   if (!std::isfinite(p->softmax_scale)) return SMLA_ERR_INVALID_ARG;
   if (p->q_stride_h < SMLA_D_QK || p->q_stride_h % 8 || p->q_stride_t < 0 || p->q_stride_t % 8)
     return SMLA_ERR_INVALID_ARG;
@@ -58,12 +71,6 @@ int check_params(const smla_params* p) {
   return SMLA_OK;
 }
 
-int head_groups_for(const smla_params* p) {
-  if (p->tiling == SMLA_TILING_PAD64) return 4;
-  if (p->num_heads <= 16) return 1;
-  if (p->num_heads <= 32) return 2;
-  return 4;
-}
 
 int splits_for(const smla_params* p, int32_t num_cus, const smla::FwdShape& sh) {
   if (p->num_splits > 0) return p->num_splits;

@@ -66,6 +66,8 @@ def test_zero_tokens_is_noop():
     (dict(num_seqs=0), B.SMLA_ERR_INVALID_ARG),
     (dict(max_blocks_per_seq=4, block_table_stride=3), B.SMLA_ERR_INVALID_ARG),
     (dict(kernel_variant=-1), B.SMLA_ERR_INVALID_ARG),
+    (dict(kernel_variant=7), B.SMLA_ERR_UNSUPPORTED),
+    (dict(kernel_variant=1, kv_format="fp8"), B.SMLA_ERR_UNSUPPORTED),
 ])
 def test_bad_params_rejected(kw, code):
     assert _fwd(_params(**kw)) == code
