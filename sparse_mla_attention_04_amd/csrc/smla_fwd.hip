@@ -52,7 +52,7 @@ constexpr float NEG_INF = -__builtin_inff();
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float REF_HEADROOM = 64.0f;   // p = 2^(x - ref) may reach 2^64 before a second pass is forced
 
-template <int HG_, int NRG_, int RT_, int NST_, int FMT_>
+template <int HG_, int NRG_, int RT_, int NST_, int FMT_, bool DSPLIT_ = false>
 struct Shape {
   static constexpr int HG = HG_;            // 16-head groups (waves per row group)
   static constexpr int NRG = NRG_;          // row groups (independent KV row streams)
@@ -72,7 +72,12 @@ struct Shape {
   static constexpr int LIST_OFF = RING_BYTES;
   static constexpr int CNT_OFF = LIST_OFF + LIST_CAP * 4;
   static constexpr int STAT_OFF = CNT_OFF + 64;
-  static constexpr int LDS_BYTES = STAT_OFF + NW * 16 * 2 * 4;
+  // DSPLIT: every wave computes P for its 16 heads, the waves exchange P
+  // through LDS, and wave w accumulates output dims [128w, 128w + 128) for all
+  // 4 head groups, so each V element is read from LDS once per tile.
+  static constexpr bool DSPLIT = DSPLIT_;
+  static constexpr int PEX_OFF = STAT_OFF + NW * 16 * 2 * 4;
+  static constexpr int LDS_BYTES = PEX_OFF + (DSPLIT ? 4 * 64 * 16 : 0);
   static constexpr int EPT = LIST_CAP / NTHR;   // index entries per thread per pass
   static constexpr bool SYNC = HG > 1;          // waves share tiles -> barrier per tile
   static_assert(RT == 16 || RT == 32, "tile rows");
@@ -82,6 +87,7 @@ struct Shape {
   static_assert(NW * 32 * 64 * 16 <= RING_BYTES, "epilogue staging must fit in the ring");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(LIST_CAP % NTHR == 0, "compaction split");
+  static_assert(!DSPLIT || (HG == 4 && NRG == 1 && RT == 32 && !FP8), "output-dim split layout");
 };
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -366,6 +372,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
       const LDS_AS uint8_t* tp = lds + toff;
       // scores S^T[row][head] for this wave's 16 heads
       f32x4 sc[S::NF];
+      bf16x8 vpre[S::DSPLIT ? 8 : 1];   // DSPLIT: V^T operands read during the score MFMAs
       f32x4 sv[S::FP8 ? S::NF : 1][4];   // fp8: block scales of the lane's accumulator rows 16f+4*g4+j
       if constexpr (S::FP8) {
 #pragma unroll
@@ -402,6 +409,42 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
           ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[1], qb[17], ar, 0, 0, 0);
           sc[f] = acc + ar;
         }
+      } else if constexpr (S::DSPLIT) {
+        // the K operands of both fragments stream through a ring of KRING reads
+        // kept ahead of the MFMAs, so LDS reads and MFMAs overlap in each wave
+        constexpr int KRING = 8;
+        bf16x8 kr[36];
+#pragma unroll
+        for (int i = 0; i < KRING; ++i)
+          kr[i] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[i / 18][(i % 18) & 1] + ((i % 18) >> 1) * S::RT * 128);
+        __builtin_amdgcn_sched_group_barrier(0x100, KRING, 0);   // the ring's first reads
+        f32x4 acc[2][2];
+#pragma unroll
+        for (int f = 0; f < 2; ++f) acc[f][0] = acc[f][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // the last ring slots fetch this wave's V^T operands for the P.V step
+        // (output dims 128*hg + 16f .., independent of the scores)
+        const LDS_AS uint8_t* tpd = tp + hg * 2 * S::RT * 128;
+#pragma unroll
+        for (int i = 0; i < 36; ++i) {
+          const int f = i / 18, kk = i % 18;
+          acc[f][kk & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[i], qb[kk], acc[f][kk & 1], 0, 0, 0);
+          const int j = i + KRING;
+          if (j < 36) {
+            kr[j] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[j / 18][(j % 18) & 1] + ((j % 18) >> 1) * S::RT * 128);
+          } else {
+            const int vf = j - 36;   // 0..7
+            const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (LDS_AS bf16x4*)(tpd + vofs[0][vf & 3] + (vf >> 2) * S::RT * 128));
+            const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (LDS_AS bf16x4*)(tpd + vofs[1][vf & 3] + (vf >> 2) * S::RT * 128));
+            vpre[vf] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // one MFMA
+          if (j < 36) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // then its LDS read(s)
+          else __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+#pragma unroll
+        for (int f = 0; f < 2; ++f) sc[f] = acc[f][0] + acc[f][1];
       } else
 #pragma unroll
       for (int f = 0; f < S::NF; ++f) {
@@ -508,6 +551,26 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
           for (int i = 0; i < 8; ++i)
             o[8 * g + i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[g & 1][i], pb, o[8 * g + i], 0, 0, 0);
         }
+      } else if constexpr (S::DSPLIT) {
+        bf16x8 pb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          pb[j] = (__bf16)pv[0][j];
+          pb[4 + j] = (__bf16)pv[1][j];
+        }
+        // publish this head group's P (already in B-operand layout), take all four
+        LDS_AS bf16x8* pex = (LDS_AS bf16x8*)(lds + S::PEX_OFF);
+        pex[hg * 64 + lane] = pb;
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        bf16x8 pall[4];
+#pragma unroll
+        for (int hf = 0; hf < 4; ++hf) pall[hf] = pex[hf * 64 + lane];
+        // P.V over this wave's 8 output fragments (V^T read during the score MFMAs), each for 4 head groups
+#pragma unroll
+        for (int f = 0; f < 8; ++f)
+#pragma unroll
+          for (int hf = 0; hf < 4; ++hf)
+            o[4 * f + hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vpre[f], pall[hf], o[4 * f + hf], 0, 0, 0);
       } else {
         bf16x8 pb;
 #pragma unroll
@@ -591,7 +654,14 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
     stat[(wave * 16 + lane) * 2 + 0] = m_run;
     stat[(wave * 16 + lane) * 2 + 1] = l_tot;
   }
-  {
+  if constexpr (S::DSPLIT) {
+    // stage as if head group hf held all 32 output fragments (layout read below)
+#pragma unroll
+    for (int f = 0; f < 8; ++f)
+#pragma unroll
+      for (int hf = 0; hf < 4; ++hf)
+        (reinterpret_cast<f32x4*>(smem) + (size_t)hf * 32 * 64)[(8 * hg + f) * 64 + lane] = o[4 * f + hf];
+  } else {
     f32x4* ost = reinterpret_cast<f32x4*>(smem) + (size_t)wave * 32 * 64;
 #pragma unroll
     for (int f = 0; f < 32; ++f) ost[f * 64 + lane] = o[f];
@@ -723,7 +793,8 @@ using V_H1_A = Shape<1, 4, 16, 2, 0>;
 using V_H1_B = Shape<1, 2, 16, 4, 0>;
 using V_H2_A = Shape<2, 2, 32, 2, 0>;
 using V_H2_B = Shape<2, 1, 32, 4, 0>;
-using V_H4_A = Shape<4, 1, 32, 4, 0>;
+using V_H4_A = Shape<4, 1, 32, 4, 0, true>;
+using V_H4_B = Shape<4, 1, 32, 4, 0>;
 using F_H1_A = Shape<1, 2, 32, 3, 1>;
 using F_H2_A = Shape<2, 1, 32, 4, 1>;
 using F_H4_A = Shape<4, 1, 32, 7, 1>;
@@ -754,7 +825,7 @@ bool fwd_shape(int kv_format, int head_groups, int variant, FwdShape* shape) {
   switch (head_groups) {
     case 1: *shape = variant == 1 ? shape_of<V_H1_B>() : shape_of<V_H1_A>(); return variant <= 1;
     case 2: *shape = variant == 1 ? shape_of<V_H2_B>() : shape_of<V_H2_A>(); return variant <= 1;
-    case 4: *shape = shape_of<V_H4_A>(); return variant == 0;
+    case 4: *shape = variant == 1 ? shape_of<V_H4_B>() : shape_of<V_H4_A>(); return variant <= 1;
     default: return false;
   }
 }
@@ -772,11 +843,10 @@ hipError_t launch_fwd(const FwdArgs& a, int kv_format, int head_groups, int vari
   switch (head_groups) {
     case 1: return variant == 1 ? launch_one<V_H1_B>(a, grid, stream) : launch_one<V_H1_A>(a, grid, stream);
     case 2: return variant == 1 ? launch_one<V_H2_B>(a, grid, stream) : launch_one<V_H2_A>(a, grid, stream);
-    case 4: return launch_one<V_H4_A>(a, grid, stream);
+    case 4: return variant == 1 ? launch_one<V_H4_B>(a, grid, stream) : launch_one<V_H4_A>(a, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }
-
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)a.T, (unsigned)((a.h * 64 + 255) / 256));
   if (a.num_splits <= 4) hipLaunchKernelGGL(smla_lse_combine<4>, grid, dim3(256), 0, stream, a);
