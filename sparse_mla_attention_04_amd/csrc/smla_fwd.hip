@@ -52,7 +52,7 @@ constexpr float NEG_INF = -__builtin_inff();
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float REF_HEADROOM = 64.0f;   // p = 2^(x - ref) may reach 2^64 before a second pass is forced
 
-template <int HG_, int NRG_, int RT_, int NST_, int FMT_, bool DSPLIT_ = false>
+template <int HG_, int NRG_, int RT_, int NST_, int FMT_, bool DSPLIT_ = false, bool PIPE_ = false>
 struct Shape {
   static constexpr int HG = HG_;            // 16-head groups (waves per row group)
   static constexpr int NRG = NRG_;          // row groups (independent KV row streams)
@@ -71,23 +71,28 @@ struct Shape {
   static constexpr int RING_BYTES = NRG * NST * TILE_BYTES;
   static constexpr int LIST_OFF = RING_BYTES;
   static constexpr int CNT_OFF = LIST_OFF + LIST_CAP * 4;
-  static constexpr int STAT_OFF = CNT_OFF + 64;
   // DSPLIT: every wave computes P for its 16 heads, the waves exchange P
   // through LDS, and wave w accumulates output dims [128w, 128w + 128) for all
   // 4 head groups, so each V element is read from LDS once per tile.
   static constexpr bool DSPLIT = DSPLIT_;
-  static constexpr int PEX_OFF = STAT_OFF + NW * 16 * 2 * 4;
-  static constexpr int LDS_BYTES = PEX_OFF + (DSPLIT ? 4 * 64 * 16 : 0);
+  // PIPE (with DSPLIT): software pipeline over tiles; the scores of tile i+1
+  // are computed while tile i's softmax runs and tile i+NST's gathers are
+  // issued, and tile i+1's V^T operands are read while tile i's P.V runs.
+  static constexpr bool PIPE = PIPE_;
+  static constexpr int PEX_OFF = CNT_OFF + 64;
+  static constexpr int STAT_OFF = PEX_OFF + (DSPLIT ? 4 * 64 * 16 : 0);
+  static constexpr int LDS_BYTES = STAT_OFF + NW * 16 * 2 * 4;
   static constexpr int EPT = LIST_CAP / NTHR;   // index entries per thread per pass
   static constexpr bool SYNC = HG > 1;          // waves share tiles -> barrier per tile
   static_assert(RT == 16 || RT == 32, "tile rows");
   static_assert(!FP8 || RT == 32, "the fp8 P.V step pairs two 16-row fragments");
   static_assert(NRH % HG == 0, "DMA groups must split evenly over the waves of a row group");
   static_assert((NST - 1) * PER <= 63, "vmcnt holds at most 63 outstanding loads");
-  static_assert(NW * 32 * 64 * 16 <= RING_BYTES, "epilogue staging must fit in the ring");
+  static_assert(NW * 32 * 64 * 16 <= STAT_OFF, "epilogue staging must fit below the statistics");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(LIST_CAP % NTHR == 0, "compaction split");
   static_assert(!DSPLIT || (HG == 4 && NRG == 1 && RT == 32 && !FP8), "output-dim split layout");
+  static_assert(!PIPE || (DSPLIT && NST >= 3 && PER == 9), "pipelined variant layout");
 };
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -132,6 +137,15 @@ __device__ __forceinline__ float wave_xor(float v, int m) { return __shfl_xor(v,
 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max over lanes l, l^16, l^32, l^48 with the gfx950 lane-swap instructions
+// (rows of 16 lanes swapped, then halves of 32), no LDS traffic
+__device__ __forceinline__ float max_xor16_32(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   __bf16 b = (__bf16)x;
@@ -606,32 +620,188 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
 #pragma unroll
     for (int kk = 0; kk < 18; ++kk) asm volatile("" : : "v"(qb[kk]));
 
-    // ---- the pipeline
-    int iss = 0;
+    if constexpr (S::PIPE) {
+      // ---- software-pipelined schedule (one tile stream, four waves):
+      //   prologue: gather tiles 0..NST-2; scores of tile 0 (gather NST-1 under it); V^T of tile 0
+      //   step i:   [tile i+1 landed, barrier]
+      //             scores of tile i+1  ||  softmax of tile i  ||  gathers of tile i+NST
+      //             P of tile i exchanged (barrier)
+      //             P.V of tile i       ||  V^T operands of tile i+1
+      // Tile i's slot is free after step i-1 (its K and V^T were read then), so
+      // the gathers of step i refill it.  Every step issues one tile's gathers
+      // (past the list they re-read its last row into a free slot), which keeps
+      // the outstanding-load count fixed.
+      constexpr int KRING = 8;
+      const uint8_t* dg = a.kv;
+      uint32_t dmb = 0;
+      auto dma_prep = [&](int itd) {
+        const int r = 8 * hg + (lane >> 3);
+        int li = itd * S::RT + r;
+        li = (li < n_valid) ? li : n_valid - 1;
+        const int slot = list[li];
+        dg = a.kv + (int64_t)slot * ROW_BYTES + ((lane & 7) ^ ((r >> 1) & 7)) * 16;
+        dmb = tile_lds(itd) + (uint32_t)hg * 1024u;
+      };
+      auto dma_line = [&](int L) {
+        constexpr uint32_t LS = S::RT * 128 - 128;
+        switch (L) {
+          case 0: dma16<0 * 128>(dg, dmb + 0 * LS); break;
+          case 1: dma16<1 * 128>(dg, dmb + 1 * LS); break;
+          case 2: dma16<2 * 128>(dg, dmb + 2 * LS); break;
+          case 3: dma16<3 * 128>(dg, dmb + 3 * LS); break;
+          case 4: dma16<4 * 128>(dg, dmb + 4 * LS); break;
+          case 5: dma16<5 * 128>(dg, dmb + 5 * LS); break;
+          case 6: dma16<6 * 128>(dg, dmb + 6 * LS); break;
+          case 7: dma16<7 * 128>(dg, dmb + 7 * LS); break;
+          default: dma16<8 * 128>(dg, dmb + 8 * LS); break;
+        }
+      };
+      auto tptr = [&](int it) { return lds + (tile_lds(it) - ring0); };
+      // online softmax of one tile (base 2, fixed exponent reference); the
+      // lane owns head n and rows 16f + 4*g4 + j; returns P in the B-operand layout
+      auto softmax = [&](int it, const f32x4* scv) -> bf16x8 {
+        const int left = n_valid - it * S::RT;
+        float x[2][4];
+        float mx = NEG_INF;
 #pragma unroll
-    for (int st = 0; st < S::NST - 1; ++st) {
-      if (iss < nit) {
-        if (iss < nt_rg) issue(iss);
-        ++iss;
-      }
-    }
-    for (int it = 0; it < nit; ++it) {
-      if constexpr (!S::SYNC) {
-        if (iss < nit) {
-          if (iss < nt_rg) issue(iss);
-          ++iss;
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float v = scv[f][j] * a.scale_log2;
+            x[f][j] = (16 * f + 4 * g4 + j < left) ? v : NEG_INF;
+            mx = fmaxf(mx, x[f][j]);
+          }
+        mx = max_xor16_32(mx);
+        m_seen = fmaxf(m_seen, mx);
+        if (m_run == NEG_INF) m_run = mx;
+        overflow |= (mx > m_run + REF_HEADROOM);
+        bf16x8 pb;
+        float psum = 0.f;
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float pj = fast_exp2(x[f][j] - m_run);
+            psum += pj;
+            pb[4 * f + j] = (__bf16)pj;
+          }
+        l_run += psum;
+        return pb;
+      };
+      // scores of tile itq (K operands through a ring of KRING reads) with the
+      // gathers of tile itd interleaved, one 128-B line per four MFMAs
+      auto scores = [&](int itq, int itd, f32x4* out) {
+        const LDS_AS uint8_t* tp = tptr(itq);
+        dma_prep(itd);   // its list entry is read before the ring starts
+        bf16x8 kr[36];
+#pragma unroll
+        for (int i = 0; i < KRING; ++i)
+          kr[i] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[i / 18][(i % 18) & 1] + ((i % 18) >> 1) * S::RT * 128);
+        __builtin_amdgcn_sched_group_barrier(0x100, KRING + 1, 0);   // the list entry and the ring's first reads
+        f32x4 acc[2][2];
+#pragma unroll
+        for (int f = 0; f < 2; ++f) acc[f][0] = acc[f][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 36; ++i) {
+          const int f = i / 18, kk = i % 18;
+          acc[f][kk & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[i], qb[kk], acc[f][kk & 1], 0, 0, 0);
+          const int j = i + KRING;
+          if (j < 36)
+            kr[j] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[j / 18][(j % 18) & 1] + ((j % 18) >> 1) * S::RT * 128);
+          if ((i & 3) == 3) dma_line(i >> 2);
+          // one MFMA, then its ring read
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (j < 36) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-      }
-      const int real = (iss < nt_rg) ? iss : nt_rg;
-      wait_tiles<S::PER, S::NST>(real - (it + 1));
-      if constexpr (S::SYNC) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f) out[f] = acc[f][0] + acc[f][1];
+      };
+      // V^T operands of tile itv for this wave's output dims 128*hg ..
+      auto read_vt = [&](int itv, int f) -> bf16x8 {
+        const LDS_AS uint8_t* tpd = tptr(itv) + hg * 2 * S::RT * 128;
+        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (LDS_AS bf16x4*)(tpd + vofs[0][f & 3] + (f >> 2) * S::RT * 128));
+        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (LDS_AS bf16x4*)(tpd + vofs[1][f & 3] + (f >> 2) * S::RT * 128));
+        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+
+      if (nit > 0) {
+#pragma unroll
+        for (int st = 0; st < S::NST - 1; ++st) {
+          dma_prep(st);
+#pragma unroll
+          for (int L = 0; L < 9; ++L) dma_line(L);
+        }
+        wait_vm<(S::NST - 2) * S::PER>();
         lds_barrier();
+        f32x4 sc[2];
+        scores(0, S::NST - 1, sc);
+        bf16x8 vpre[8];
+#pragma unroll
+        for (int f = 0; f < 8; ++f) vpre[f] = read_vt(0, f);
+        LDS_AS bf16x8* pex = (LDS_AS bf16x8*)(lds + S::PEX_OFF);
+        for (int it = 0; it < nit; ++it) {
+          wait_vm<(S::NST - 2) * S::PER>();   // tile it+1 has landed (this wave's share)
+          // every wave's reads of tile it (its V^T operands) have completed
+          // before any gather refills that slot
+          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          bf16x8 pb;
+          f32x4 scn[2];
+          if (it + 1 < nit) {
+            pb = softmax(it, sc);
+            scores(it + 1, it + S::NST, scn);
+          } else {
+            pb = softmax(it, sc);
+            scn[0] = scn[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+          // publish this head group's P, take all four
+          pex[hg * 64 + lane] = pb;
+          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          bf16x8 pall[4];
+#pragma unroll
+          for (int hf = 0; hf < 4; ++hf) pall[hf] = pex[hf * 64 + lane];
+          // P.V of tile it over this wave's 8 output fragments x 4 head groups;
+          // each fragment's V^T registers are refilled from tile it+1 once used
+#pragma unroll
+          for (int f = 0; f < 8; ++f) {
+#pragma unroll
+            for (int hf = 0; hf < 4; ++hf)
+              o[4 * f + hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vpre[f], pall[hf], o[4 * f + hf], 0, 0, 0);
+            vpre[f] = read_vt(it + 1, f);
+          }
+          sc[0] = scn[0];
+          sc[1] = scn[1];
+        }
+      }
+    } else {
+      // ---- the pipeline
+      int iss = 0;
+  #pragma unroll
+      for (int st = 0; st < S::NST - 1; ++st) {
         if (iss < nit) {
           if (iss < nt_rg) issue(iss);
           ++iss;
         }
       }
-      if (it < nt_rg) compute(it);
+      for (int it = 0; it < nit; ++it) {
+        if constexpr (!S::SYNC) {
+          if (iss < nit) {
+            if (iss < nt_rg) issue(iss);
+            ++iss;
+          }
+        }
+        const int real = (iss < nt_rg) ? iss : nt_rg;
+        wait_tiles<S::PER, S::NST>(real - (it + 1));
+        if constexpr (S::SYNC) {
+          lds_barrier();
+          if (iss < nit) {
+            if (iss < nt_rg) issue(iss);
+            ++iss;
+          }
+        }
+        if (it < nt_rg) compute(it);
+      }
     }
     wait_vm<0>();
     __syncthreads();   // the list is rewritten by the next pass
@@ -793,8 +963,9 @@ using V_H1_A = Shape<1, 4, 16, 2, 0>;
 using V_H1_B = Shape<1, 2, 16, 4, 0>;
 using V_H2_A = Shape<2, 2, 32, 2, 0>;
 using V_H2_B = Shape<2, 1, 32, 4, 0>;
-using V_H4_A = Shape<4, 1, 32, 4, 0, true>;
+using V_H4_A = Shape<4, 1, 32, 4, 0, true, true>;
 using V_H4_B = Shape<4, 1, 32, 4, 0>;
+using V_H4_C = Shape<4, 1, 32, 4, 0, true>;
 using F_H1_A = Shape<1, 2, 32, 3, 1>;
 using F_H2_A = Shape<2, 1, 32, 4, 1>;
 using F_H4_A = Shape<4, 1, 32, 7, 1>;
@@ -825,7 +996,9 @@ bool fwd_shape(int kv_format, int head_groups, int variant, FwdShape* shape) {
   switch (head_groups) {
     case 1: *shape = variant == 1 ? shape_of<V_H1_B>() : shape_of<V_H1_A>(); return variant <= 1;
     case 2: *shape = variant == 1 ? shape_of<V_H2_B>() : shape_of<V_H2_A>(); return variant <= 1;
-    case 4: *shape = variant == 1 ? shape_of<V_H4_B>() : shape_of<V_H4_A>(); return variant <= 1;
+    case 4:
+      *shape = variant == 2 ? shape_of<V_H4_C>() : variant == 1 ? shape_of<V_H4_B>() : shape_of<V_H4_A>();
+      return variant <= 2;
     default: return false;
   }
 }
@@ -843,7 +1016,10 @@ hipError_t launch_fwd(const FwdArgs& a, int kv_format, int head_groups, int vari
   switch (head_groups) {
     case 1: return variant == 1 ? launch_one<V_H1_B>(a, grid, stream) : launch_one<V_H1_A>(a, grid, stream);
     case 2: return variant == 1 ? launch_one<V_H2_B>(a, grid, stream) : launch_one<V_H2_A>(a, grid, stream);
-    case 4: return variant == 1 ? launch_one<V_H4_B>(a, grid, stream) : launch_one<V_H4_A>(a, grid, stream);
+    case 4:
+      return variant == 2   ? launch_one<V_H4_C>(a, grid, stream)
+             : variant == 1 ? launch_one<V_H4_B>(a, grid, stream)
+                            : launch_one<V_H4_A>(a, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -44,7 +44,8 @@ def test_mini_heads(h):
 
 @pytest.mark.parametrize("h,tiling,variant", [(8, "pad64", 0), (16, "pad64", 0), (8, "native", 1),
                                                (16, "native", 1), (32, "native", 1), (24, "native", 1),
-                                               (64, "native", 1), (40, "native", 1), (8, "pad64", 1)])
+                                               (64, "native", 1), (40, "native", 1), (8, "pad64", 1),
+                                               (64, "native", 2), (48, "native", 2), (16, "pad64", 2)])
 def test_mini_tilings_and_variants(h, tiling, variant):
     say("mini tiling", h, tiling, variant)
     c = G.make_mini(seed=22, num_heads=h, topk=300)
