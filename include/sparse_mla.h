@@ -117,10 +117,9 @@ typedef struct smla_params {
   float softmax_scale;         /* multiplies q.k (e.g. 1/sqrt(576)); finite           */
   int32_t tiling;              /* SMLA_TILING_*                                       */
   int32_t num_splits;          /* 0 = automatic; n >= 1 forces n KV splits per row    */
-  int32_t kernel_variant;      /* 0 = default pipeline shape; 1 = alternative shape;  */
-                               /* 2 = second alternative (bf16, h > 32 only); others  */
-                               /* -> SMLA_ERR_UNSUPPORTED (tuning knob, see smla_plan; */
-                               /* same results to tolerance)                          */
+  int32_t kernel_variant;      /* 0 = default pipeline shape; 1 = alternative shape   */
+                               /* (bf16 only; others -> SMLA_ERR_UNSUPPORTED); a      */
+                               /* tuning knob, see smla_plan; same results to tol.    */
 } smla_params;
 
 /* Read-only description of how a call with these parameters is executed. */

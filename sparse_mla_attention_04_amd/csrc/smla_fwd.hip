@@ -93,6 +93,7 @@ struct Shape {
   static_assert(LIST_CAP % NTHR == 0, "compaction split");
   static_assert(!DSPLIT || (HG == 4 && NRG == 1 && RT == 32 && !FP8), "output-dim split layout");
   static_assert(!PIPE || (DSPLIT && NST >= 3 && PER == 9), "pipelined variant layout");
+  static_assert(!DSPLIT || PIPE, "the output-dim split runs in the pipelined schedule");
 };
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -175,6 +176,19 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
   return bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
 }
 
+// XOR swizzle of the 16-byte chunks of tile row r (3 bits), chosen per cache
+// format from LDS bank-conflict counts measured on gfx950 for each access
+// pattern of the kernels:
+//   bf16 tiles (16-row K operand reads of one chunk; 4-row x 2-chunk
+//     transposing V reads): r & 7 leaves both conflict-free;
+//   fp8 tiles (transposing reads of rows 4g + j and 16 + 4g + j): rows r and
+//     r + 16 must differ, which r & 7 does not give.
+template <bool FP8>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (FP8) return (((r >> 1) & 1) << 1) | (((r >> 2) & 1) << 2) | (((r >> 3) ^ (r >> 4)) & 1);
+  else return r & 7;
+}
+
 // Translate one index entry to a physical cache row; -1 when skipped.
 __device__ __forceinline__ int translate(const FwdArgs& a, int j, int seq_ok, int64_t bt_row) {
   if (j < 0) return -1;
@@ -185,6 +199,44 @@ __device__ __forceinline__ int translate(const FwdArgs& a, int j, int seq_ok, in
   const int page = a.block_table[bt_row + blk];
   if (page < 0 || page >= a.num_pages) return -1;
   return (page << a.page_shift) | (j & ((1 << a.page_shift) - 1));
+}
+
+// Translate a thread's EPT raw index entries, compact the surviving rows in
+// order into list[] (a wave-level prefix sum, then the waves' offsets), and
+// return the chunk's count.  Two work-group barriers.
+template <int NW, int EPT>
+__device__ __forceinline__ int compact_chunk(const FwdArgs& a, const int (&raw)[EPT], int seq_ok, int64_t bt_row,
+                                             int* list, int* wcnt, int wave, int lane) {
+  int sl[EPT];
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int s = translate(a, raw[i], seq_ok, bt_row);
+    sl[i] = s;
+    cnt += (s >= 0);
+  }
+  int incl = cnt;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
+  }
+  if (lane == 63) wcnt[wave] = incl;
+  __syncthreads();
+  int base = 0, n_valid = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int c = wcnt[w];
+    base += (w < wave) ? c : 0;
+    n_valid += c;
+  }
+  int pos = base + incl - cnt;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    if (sl[i] >= 0) { list[pos] = sl[i]; ++pos; }
+  }
+  __syncthreads();
+  return n_valid;
 }
 
 template <class S>
@@ -210,17 +262,17 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
   const int g4 = lane >> 4, n = lane & 15;
 
   // ---- per-lane LDS offsets inside a tile
-  // tile layout: position(r, c) = (c / 8) * RT * 8 + r * 8 + ((c % 8) ^ ((r >> 1) & 7)), 16 B each
+  // tile layout: position(r, c) = (c / 8) * RT * 8 + r * 8 + ((c % 8) ^ swz(r)), 16 B each
   uint32_t kofs[S::NF][2];     // K operand: row 16f+n, chunk 4*kk+g4
   uint32_t vofs[S::NF][4];     // V^T operand (transposing read): row 16f+4*g4+(n>>2), dims 4*(n&3)
 #pragma unroll
   for (int f = 0; f < S::NF; ++f) {
     const int r = 16 * f + n;
-    const int sw = (r >> 1) & 7;
+    const int sw = swz<S::FP8>(r);
 #pragma unroll
     for (int p = 0; p < 2; ++p) kofs[f][p] = (uint32_t)(r * 8 + ((4 * p + g4) ^ sw)) * 16u;
     const int rv = 16 * f + 4 * g4 + (n >> 2);
-    const int swv = (rv >> 1) & 7;
+    const int swv = swz<S::FP8>(rv);
     const int cq = n & 3;
 #pragma unroll
     for (int p = 0; p < 4; ++p)
@@ -228,20 +280,11 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
   }
 
   // fp8 rows: 40 chunks of 16 B ([512 codes | 64 bf16 rope]) laid out like the bf16 tile
-  uint32_t k8ofs[S::FP8 ? S::NF : 1][4];   // latent codes: row 16f+n, 8 B at dims 32*kk + 8*g4
   uint32_t tr8ofs[S::FP8 ? 8 : 1];         // transposing fp8 read: row kmap(g4, n>>1), 8 B at dims 16f + 8*(n&1)
   if constexpr (S::FP8) {
-#pragma unroll
-    for (int f = 0; f < S::NF; ++f) {
-      const int r = 16 * f + n;
-      const int sw = (r >> 1) & 7;
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-        k8ofs[f][p] = (uint32_t)(r * 8 + ((2 * p + (g4 >> 1)) ^ sw)) * 16u + (uint32_t)(g4 & 1) * 8u;
-    }
     const int kq = n >> 1;
     const int rr = (kq < 4) ? 4 * g4 + kq : 16 + 4 * g4 + (kq - 4);
-    const int swr = (rr >> 1) & 7;
+    const int swr = swz<S::FP8>(rr);
 #pragma unroll
     for (int p = 0; p < 8; ++p) tr8ofs[p] = (uint32_t)(rr * 8 + (p ^ swr)) * 16u + (uint32_t)(n & 1) * 8u;
   }
@@ -278,7 +321,16 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
     if (head < a.h) {
       const uint16_t* qp = a.q + (int64_t)t * a.q_st + (int64_t)head * a.q_sh + 8 * g4;
 #pragma unroll
-      for (int kk = 0; kk < 18; ++kk) qb[kk] = *reinterpret_cast<const bf16x8*>(qp + 32 * kk);
+      for (int kk = 0; kk < 18; ++kk) {
+        // fp8 latent k-steps take their dims in the order the 16-byte code reads
+        // deliver them: step (block b, s) of a lane covers dims
+        // 128b + 64(s >> 1) + 16*g4 + 8(s & 1) .. +7 (a permutation of the block's
+        // dims, applied to q and k alike); the rope steps keep 32kk + 8*g4
+        const int off = (S::FP8 && kk < 16)
+                            ? 128 * (kk >> 2) + 64 * ((kk & 3) >> 1) + 8 * g4 + 8 * (kk & 1)
+                            : 32 * kk;
+        qb[kk] = *reinterpret_cast<const bf16x8*>(qp + off);
+      }
     } else {
 #pragma unroll
       for (int kk = 0; kk < 18; ++kk) qb[kk] = bf16x8{};
@@ -299,36 +351,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
   for (int64_t cs = c0; cs < c1; cs += LIST_CAP) {
     const int64_t ce = (cs + LIST_CAP < c1) ? cs + LIST_CAP : c1;
     if (cs != c0 || pass != 0) load_raw(cs, ce);
-    // ---- compaction (order preserved)
-    int sl[S::EPT];
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < S::EPT; ++i) {
-      const int s = translate(a, raw[i], seq_ok, bt_row);
-      sl[i] = s;
-      cnt += (s >= 0);
-    }
-    int incl = cnt;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int v = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += v;
-    }
-    if (lane == 63) wcnt[wave] = incl;
-    __syncthreads();
-    int base = 0, n_valid = 0;
-#pragma unroll
-    for (int w = 0; w < S::NW; ++w) {
-      const int c = wcnt[w];
-      base += (w < wave) ? c : 0;
-      n_valid += c;
-    }
-    int pos = base + incl - cnt;
-#pragma unroll
-    for (int i = 0; i < S::EPT; ++i) {
-      if (sl[i] >= 0) { list[pos] = sl[i]; ++pos; }
-    }
-    __syncthreads();
+    const int n_valid = compact_chunk<S::NW, S::EPT>(a, raw, seq_ok, bt_row, list, wcnt, wave, lane);
 
     // ---- tiles: tile i belongs to row group i % NRG
     const int ntile = (n_valid + S::RT - 1) / S::RT;
@@ -348,7 +371,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         int li = tstart + r;
         li = (li < n_valid) ? li : n_valid - 1;           // tail rows repeat the last valid row
         const int slot = list[li];
-        const int q = (lane & 7) ^ ((r >> 1) & 7);
+        const int q = (lane & 7) ^ swz<S::FP8>(r);
         const uint8_t* g = a.kv + row_offset<S::FP8>(a, slot) + q * 16;
         const uint32_t mb = tl + (uint32_t)rh * 1024u;
         // line L of the row lands at tile position L*RT*8 + rh*64 + lane
@@ -386,7 +409,6 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
       const LDS_AS uint8_t* tp = lds + toff;
       // scores S^T[row][head] for this wave's 16 heads
       f32x4 sc[S::NF];
-      bf16x8 vpre[S::DSPLIT ? 8 : 1];   // DSPLIT: V^T operands read during the score MFMAs
       f32x4 sv[S::FP8 ? S::NF : 1][4];   // fp8: block scales of the lane's accumulator rows 16f+4*g4+j
       if constexpr (S::FP8) {
 #pragma unroll
@@ -399,66 +421,44 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
           // latent: 16 k-steps of 8 fp8 codes per lane, dequantised exactly to
           // bf16; each 128-dim block accumulates separately and is scaled in fp32
           typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+          // 16 codes per lane per read: k-steps (b, 2m) and (b, 2m + 1) of block b
+          u32x4 kq[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            kq[i] = *reinterpret_cast<const LDS_AS u32x4*>(tp + kofs[f][i & 1] + (i >> 1) * S::RT * 128);
           u32x2 kw[16];
 #pragma unroll
-          for (int kk = 0; kk < 16; ++kk)
-            kw[kk] = *reinterpret_cast<const LDS_AS u32x2*>(tp + k8ofs[f][kk & 3] + (kk >> 2) * S::RT * 128);
+          for (int kk = 0; kk < 16; ++kk) {
+            const u32x4 v = kq[2 * (kk >> 2) + ((kk & 3) >> 1)];
+            kw[kk] = (kk & 1) ? u32x2{v[2], v[3]} : u32x2{v[0], v[1]};
+          }
           bf16x8 kr[2];
 #pragma unroll
           for (int kk = 0; kk < 2; ++kk)
             kr[kk] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[f][kk] + 4 * S::RT * 128);
           __builtin_amdgcn_sched_barrier(0);
+          // one accumulation chain per 128-dim block (interleaved, so consecutive
+          // MFMAs are independent) and one per rope k-step
+          f32x4 ab[4], ar[2];
+#pragma unroll
+          for (int blk = 0; blk < 4; ++blk) ab[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+          ar[0] = ar[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk) {
+              const int kk = 4 * blk + ks;
+              ab[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(kw[kk][0], kw[kk][1]), qb[kk], ab[blk], 0, 0, 0);
+            }
+            if (ks < 2) ar[ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks], qb[16 + ks], ar[ks], 0, 0, 0);
+          }
           f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int blk = 0; blk < 4; ++blk) {
-            f32x4 ab = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
-            for (int kk = 4 * blk; kk < 4 * blk + 4; ++kk)
-              ab = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(kw[kk][0], kw[kk][1]), qb[kk], ab, 0, 0, 0);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[j] += ab[j] * sv[f][j][blk];
-          }
-          f32x4 ar = f32x4{0.f, 0.f, 0.f, 0.f};
-          ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[0], qb[16], ar, 0, 0, 0);
-          ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[1], qb[17], ar, 0, 0, 0);
-          sc[f] = acc + ar;
+            for (int j = 0; j < 4; ++j) acc[j] += ab[blk][j] * sv[f][j][blk];
+          sc[f] = acc + (ar[0] + ar[1]);
         }
-      } else if constexpr (S::DSPLIT) {
-        // the K operands of both fragments stream through a ring of KRING reads
-        // kept ahead of the MFMAs, so LDS reads and MFMAs overlap in each wave
-        constexpr int KRING = 8;
-        bf16x8 kr[36];
-#pragma unroll
-        for (int i = 0; i < KRING; ++i)
-          kr[i] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[i / 18][(i % 18) & 1] + ((i % 18) >> 1) * S::RT * 128);
-        __builtin_amdgcn_sched_group_barrier(0x100, KRING, 0);   // the ring's first reads
-        f32x4 acc[2][2];
-#pragma unroll
-        for (int f = 0; f < 2; ++f) acc[f][0] = acc[f][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // the last ring slots fetch this wave's V^T operands for the P.V step
-        // (output dims 128*hg + 16f .., independent of the scores)
-        const LDS_AS uint8_t* tpd = tp + hg * 2 * S::RT * 128;
-#pragma unroll
-        for (int i = 0; i < 36; ++i) {
-          const int f = i / 18, kk = i % 18;
-          acc[f][kk & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[i], qb[kk], acc[f][kk & 1], 0, 0, 0);
-          const int j = i + KRING;
-          if (j < 36) {
-            kr[j] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[j / 18][(j % 18) & 1] + ((j % 18) >> 1) * S::RT * 128);
-          } else {
-            const int vf = j - 36;   // 0..7
-            const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (LDS_AS bf16x4*)(tpd + vofs[0][vf & 3] + (vf >> 2) * S::RT * 128));
-            const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (LDS_AS bf16x4*)(tpd + vofs[1][vf & 3] + (vf >> 2) * S::RT * 128));
-            vpre[vf] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // one MFMA
-          if (j < 36) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // then its LDS read(s)
-          else __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-#pragma unroll
-        for (int f = 0; f < 2; ++f) sc[f] = acc[f][0] + acc[f][1];
       } else
 #pragma unroll
       for (int f = 0; f < S::NF; ++f) {
@@ -469,13 +469,15 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         for (int kk = 0; kk < 18; ++kk)
           kb[kk] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[f][kk & 1] + (kk >> 1) * S::RT * 128);
         __builtin_amdgcn_sched_barrier(0);
-        f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+        // six independent accumulation chains: a dependent MFMA waits for its
+        // predecessor's result, so consecutive MFMAs go to different chains
+        f32x4 acc[6];
 #pragma unroll
-        for (int kk = 0; kk < 18; kk += 2) {
-          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qb[kk], acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk + 1], qb[kk + 1], acc1, 0, 0, 0);
-        }
-        sc[f] = acc0 + acc1;
+        for (int c = 0; c < 6; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 18; ++kk)
+          acc[kk % 6] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qb[kk], acc[kk % 6], 0, 0, 0);
+        sc[f] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + (acc[4] + acc[5]);
       }
       // online softmax (base 2); lane owns head n, rows 16f + 4*g4 + j
       const int left = n_valid - tstart;
@@ -565,26 +567,6 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
           for (int i = 0; i < 8; ++i)
             o[8 * g + i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[g & 1][i], pb, o[8 * g + i], 0, 0, 0);
         }
-      } else if constexpr (S::DSPLIT) {
-        bf16x8 pb;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          pb[j] = (__bf16)pv[0][j];
-          pb[4 + j] = (__bf16)pv[1][j];
-        }
-        // publish this head group's P (already in B-operand layout), take all four
-        LDS_AS bf16x8* pex = (LDS_AS bf16x8*)(lds + S::PEX_OFF);
-        pex[hg * 64 + lane] = pb;
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        bf16x8 pall[4];
-#pragma unroll
-        for (int hf = 0; hf < 4; ++hf) pall[hf] = pex[hf * 64 + lane];
-        // P.V over this wave's 8 output fragments (V^T read during the score MFMAs), each for 4 head groups
-#pragma unroll
-        for (int f = 0; f < 8; ++f)
-#pragma unroll
-          for (int hf = 0; hf < 4; ++hf)
-            o[4 * f + hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vpre[f], pall[hf], o[4 * f + hf], 0, 0, 0);
       } else {
         bf16x8 pb;
 #pragma unroll
@@ -639,7 +621,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         int li = itd * S::RT + r;
         li = (li < n_valid) ? li : n_valid - 1;
         const int slot = list[li];
-        dg = a.kv + (int64_t)slot * ROW_BYTES + ((lane & 7) ^ ((r >> 1) & 7)) * 16;
+        dg = a.kv + (int64_t)slot * ROW_BYTES + ((lane & 7) ^ swz<S::FP8>(r)) * 16;
         dmb = tile_lds(itd) + (uint32_t)hg * 1024u;
       };
       auto dma_line = [&](int L) {
@@ -693,28 +675,33 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
       auto scores = [&](int itq, int itd, f32x4* out) {
         const LDS_AS uint8_t* tp = tptr(itq);
         dma_prep(itd);   // its list entry is read before the ring starts
+        // MFMA i is (fragment i & 1, k-step i >> 1); it accumulates into chain
+        // (fragment, k-step mod 4), so each of the 8 chains is fed every 8th MFMA
+        // and no MFMA waits for its predecessor's result
         bf16x8 kr[36];
 #pragma unroll
         for (int i = 0; i < KRING; ++i)
-          kr[i] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[i / 18][(i % 18) & 1] + ((i % 18) >> 1) * S::RT * 128);
+          kr[i] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[i & 1][(i >> 1) & 1] + (i >> 2) * S::RT * 128);
         __builtin_amdgcn_sched_group_barrier(0x100, KRING + 1, 0);   // the list entry and the ring's first reads
-        f32x4 acc[2][2];
+        f32x4 acc[2][4];
 #pragma unroll
-        for (int f = 0; f < 2; ++f) acc[f][0] = acc[f][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[f][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 36; ++i) {
-          const int f = i / 18, kk = i % 18;
-          acc[f][kk & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[i], qb[kk], acc[f][kk & 1], 0, 0, 0);
+          const int f = i & 1, kk = i >> 1;
+          acc[f][kk & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[i], qb[kk], acc[f][kk & 3], 0, 0, 0);
           const int j = i + KRING;
           if (j < 36)
-            kr[j] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[j / 18][(j % 18) & 1] + ((j % 18) >> 1) * S::RT * 128);
+            kr[j] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[j & 1][(j >> 1) & 1] + (j >> 2) * S::RT * 128);
           if ((i & 3) == 3) dma_line(i >> 2);
           // one MFMA, then its ring read
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           if (j < 36) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
 #pragma unroll
-        for (int f = 0; f < 2; ++f) out[f] = acc[f][0] + acc[f][1];
+        for (int f = 0; f < 2; ++f) out[f] = (acc[f][0] + acc[f][1]) + (acc[f][2] + acc[f][3]);
       };
       // V^T operands of tile itv for this wave's output dims 128*hg ..
       auto read_vt = [&](int itv, int f) -> bf16x8 {
@@ -889,6 +876,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
   }
 }
 
+
 // Merge the KV splits of each query row by their lse, in split order.
 // Thread = (row, head, 8 output dims); SMAX > 0 unrolls the split loop so the
 // loads of all splits are in flight together (SMAX = 0: any split count).
@@ -965,7 +953,6 @@ using V_H2_A = Shape<2, 2, 32, 2, 0>;
 using V_H2_B = Shape<2, 1, 32, 4, 0>;
 using V_H4_A = Shape<4, 1, 32, 4, 0, true, true>;
 using V_H4_B = Shape<4, 1, 32, 4, 0>;
-using V_H4_C = Shape<4, 1, 32, 4, 0, true>;
 using F_H1_A = Shape<1, 2, 32, 3, 1>;
 using F_H2_A = Shape<2, 1, 32, 4, 1>;
 using F_H4_A = Shape<4, 1, 32, 7, 1>;
@@ -997,8 +984,8 @@ bool fwd_shape(int kv_format, int head_groups, int variant, FwdShape* shape) {
     case 1: *shape = variant == 1 ? shape_of<V_H1_B>() : shape_of<V_H1_A>(); return variant <= 1;
     case 2: *shape = variant == 1 ? shape_of<V_H2_B>() : shape_of<V_H2_A>(); return variant <= 1;
     case 4:
-      *shape = variant == 2 ? shape_of<V_H4_C>() : variant == 1 ? shape_of<V_H4_B>() : shape_of<V_H4_A>();
-      return variant <= 2;
+      *shape = variant == 1 ? shape_of<V_H4_B>() : shape_of<V_H4_A>();
+      return variant <= 1;
     default: return false;
   }
 }
@@ -1016,10 +1003,7 @@ hipError_t launch_fwd(const FwdArgs& a, int kv_format, int head_groups, int vari
   switch (head_groups) {
     case 1: return variant == 1 ? launch_one<V_H1_B>(a, grid, stream) : launch_one<V_H1_A>(a, grid, stream);
     case 2: return variant == 1 ? launch_one<V_H2_B>(a, grid, stream) : launch_one<V_H2_A>(a, grid, stream);
-    case 4:
-      return variant == 2   ? launch_one<V_H4_C>(a, grid, stream)
-             : variant == 1 ? launch_one<V_H4_B>(a, grid, stream)
-                            : launch_one<V_H4_A>(a, grid, stream);
+    case 4: return variant == 1 ? launch_one<V_H4_B>(a, grid, stream) : launch_one<V_H4_A>(a, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

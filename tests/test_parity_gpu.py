@@ -45,7 +45,7 @@ def test_mini_heads(h):
 @pytest.mark.parametrize("h,tiling,variant", [(8, "pad64", 0), (16, "pad64", 0), (8, "native", 1),
                                                (16, "native", 1), (32, "native", 1), (24, "native", 1),
                                                (64, "native", 1), (40, "native", 1), (8, "pad64", 1),
-                                               (64, "native", 2), (48, "native", 2), (16, "pad64", 2)])
+                                               (48, "native", 1), (16, "pad64", 1)])
 def test_mini_tilings_and_variants(h, tiling, variant):
     say("mini tiling", h, tiling, variant)
     c = G.make_mini(seed=22, num_heads=h, topk=300)
@@ -356,3 +356,42 @@ def test_c5_fp8_sampled():
     out, lse = to_np(*run_gpu(dev))
     rows = _sample_rows(c, 48, seed=5)
     check(out[rows], lse[rows], *oracle(c, rows=rows), what="c5")
+
+
+def test_graph_replay_matches_eager():
+    """A captured call on the split path (attention kernel + merge kernel)
+    replays bit for bit, with unrelated eager work between the replays."""
+    say("graph replay")
+    c = G.make_mini(seed=41, num_heads=8, topk=300)
+    dev = Dev(c)
+    T, h = c.num_tokens, c.num_heads
+    out = torch.empty((T, h, 512), dtype=torch.bfloat16, device=dev.q.device)
+    lse = torch.empty((T, h), dtype=torch.float32, device=dev.q.device)
+    p = B.params_for(dev.q, dev.kv, dev.idx, out, lse, topk=c.topk, scale=c.scale, block_table=dev.bt,
+                     token_seq=dev.ts, num_splits=3)
+    ws = B.workspace_for(p, dev.q.device)
+
+    def call():
+        B.fwd(dev.q, dev.kv, dev.idx, out, lse, topk=c.topk, scale=c.scale, workspace=ws, block_table=dev.bt,
+              token_seq=dev.ts, params=p)
+
+    call()
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(3):
+        out.fill_(7.0)
+        lse.fill_(7.0)
+        float(torch.randn(1 << 20, device=dev.q.device).sum())   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), "replay %d differs" % rep
+    check(*to_np(out, lse), *oracle(c), what="graph replay")
