@@ -8,8 +8,11 @@ compaction + gather + QK^T + softmax + PV + split merge when the plan splits).
 Inputs are resident in HBM before timing starts.  K steps are timed with HIP
 events on the stream the library launches on, bracketed by device syncs.
 Prints ONE JSON line: throughput in query-tokens/s, the dominant kernel's
-roofline (per-launch durations from events around each launch), and the CPU
-oracle timed on a bounded sample of the same workload on this host.
+roofline (per-launch durations from events around each launch), the same
+step replayed from a HIP graph (checked bit for bit against the eager
+result), the kernel after evicting the caches (1 GiB read between launches),
+and the CPU oracle timed on a bounded sample of the same workload on this
+host.
 
 Workloads (synthetic, seeded; `--workload`):
   c2_decode (default)  32 rows x 1 query, h=8, 16384-token contexts
@@ -46,6 +49,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--cold-launches", type=int, default=50)
+    ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--copy-reference", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -192,13 +196,55 @@ def main():
         kernel_only()
         b.record()
     torch.cuda.synchronize()
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    kern_all = np.array([a.elapsed_time(b) for a, b in evs])
+    kern_ms = float(np.mean(kern_all))
 
-    # ---- same kernel after evicting caches (1 GiB written between launches, not timed)
-    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    # ---- the same step replayed from a HIP graph (launch overhead of the
+    #      serving setting); every replay must reproduce the eager result bit for bit
+    graph = None
+    if not args.no_graph:
+        step()
+        torch.cuda.synchronize()
+        ref_out, ref_lse = out.clone(), lse.clone()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(2):
+                step()
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(g):
+            step()
+        checked = 0
+        for _ in range(3):
+            out.zero_()
+            lse.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            if not (torch.equal(out, ref_out) and torch.equal(lse, ref_lse)):
+                raise SystemExit("graph replay differs from the eager result")
+            checked += 1
+        for _ in range(args.warmup):
+            g.replay()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        g0.record()
+        for _ in range(args.steps):
+            g.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        gms = g0.elapsed_time(g1) / args.steps
+        graph = {"ms_per_step": round(gms, 6), "query_tokens_per_s": round(T / (gms * 1e-3), 1),
+                 "replays_checked_bitwise": checked}
+        del g
+
+    # ---- same kernel after evicting caches (1 GiB read between launches, not timed;
+    #      reading leaves no dirty lines behind that the kernel would have to write back)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     cold = []
     for _ in range(args.cold_launches):
-        flush.fill_(1.0)
+        flush.sum()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         kernel_only()
@@ -227,6 +273,7 @@ def main():
     roof["traffic_note"] = traffic_note
     roof["kernel"] = "smla_fwd" + ("" if pl.num_splits == 1 else " (split partials)")
     roof["kernel_us"] = round(kern_ms * 1e3, 2)
+    roof["kernel_us_p10_p50_p90"] = [round(float(np.percentile(kern_all, q)) * 1e3, 2) for q in (10, 50, 90)]
     roof["algorithmic_bytes"] = gathered
     roof["algorithmic_flops"] = flops
 
@@ -251,10 +298,11 @@ def main():
         "mfma_frac_per_step": round(flops / (ms_per_step * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 5),
         "wall_s_timed": round(wall, 4),
         "roofline": roof,
+        "graph": graph,
         "cold_cache": {"kernel_us_median": round(cold_ms * 1e3, 2),
                        "gathered_GBps": round(gathered / (cold_ms * 1e-3) / 1e9, 1),
                        "hbm_frac": round(gathered / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                       "note": "1 GiB written between launches to evict L2 and MALL"},
+                       "note": "1 GiB read between launches to evict L2 and MALL"},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)

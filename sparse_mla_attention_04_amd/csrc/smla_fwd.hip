@@ -52,7 +52,8 @@ constexpr float NEG_INF = -__builtin_inff();
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float REF_HEADROOM = 64.0f;   // p = 2^(x - ref) may reach 2^64 before a second pass is forced
 
-template <int HG_, int NRG_, int RT_, int NST_, int FMT_, bool DSPLIT_ = false, bool PIPE_ = false>
+template <int HG_, int NRG_, int RT_, int NST_, int FMT_, bool DSPLIT_ = false, bool PIPE_ = false,
+          bool PAIR_ = false>
 struct Shape {
   static constexpr int HG = HG_;            // 16-head groups (waves per row group)
   static constexpr int NRG = NRG_;          // row groups (independent KV row streams)
@@ -79,8 +80,17 @@ struct Shape {
   // are computed while tile i's softmax runs and tile i+NST's gathers are
   // issued, and tile i+1's V^T operands are read while tile i's P.V runs.
   static constexpr bool PIPE = PIPE_;
+  // PAIR (fp8, h <= 16): the two waves of a row stream share its tiles; wave
+  // hp forms the scores and softmax of the tile's rows 16hp .. 16hp + 15 and
+  // accumulates output dims [256hp, 256hp + 256) over all 32 rows, the scaled
+  // P of the 4 dim blocks being exchanged through LDS.  The pair shares one
+  // exponent reference.
+  static constexpr bool PAIR = PAIR_;
+  static constexpr int HEAD_GROUPS = PAIR ? 1 : HG;   // 16-head groups the shape covers
   static constexpr int PEX_OFF = CNT_OFF + 64;
-  static constexpr int STAT_OFF = PEX_OFF + (DSPLIT ? 4 * 64 * 16 : 0);
+  static constexpr int PEX_BYTES = DSPLIT ? 4 * 64 * 16 : PAIR ? NRG * 4 * 64 * 16 : 0;
+  static constexpr int MEX_OFF = PEX_OFF + PEX_BYTES;
+  static constexpr int STAT_OFF = MEX_OFF + (PAIR ? NW * 64 * 4 : 0);
   static constexpr int LDS_BYTES = STAT_OFF + NW * 16 * 2 * 4;
   static constexpr int EPT = LIST_CAP / NTHR;   // index entries per thread per pass
   static constexpr bool SYNC = HG > 1;          // waves share tiles -> barrier per tile
@@ -94,6 +104,7 @@ struct Shape {
   static_assert(!DSPLIT || (HG == 4 && NRG == 1 && RT == 32 && !FP8), "output-dim split layout");
   static_assert(!PIPE || (DSPLIT && NST >= 3 && PER == 9), "pipelined variant layout");
   static_assert(!DSPLIT || PIPE, "the output-dim split runs in the pipelined schedule");
+  static_assert(!PAIR || (FP8 && HG == 2 && RT == 32 && !DSPLIT), "row/dim-split pair layout");
 };
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -317,7 +328,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
   //      lane (g4, n) holds head hg*16+n, dims 32*kk + 8*g4 .. +7
   bf16x8 qb[18];
   {
-    const int head = hg * 16 + n;
+    const int head = (S::PAIR ? 0 : hg) * 16 + n;
     if (head < a.h) {
       const uint16_t* qp = a.q + (int64_t)t * a.q_st + (int64_t)head * a.q_sh + 8 * g4;
 #pragma unroll
@@ -598,6 +609,104 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
       }
     };
 
+    // fp8 row/dim-split pair: every wave runs this each step (barriers inside);
+    // `active` is false once the row stream has no tile at this step
+    auto compute_pair = [&](int it, bool active) {
+      if constexpr (S::PAIR) {
+        const int tstart = (rg + S::NRG * it) * S::RT;
+        const LDS_AS uint8_t* tp = lds + (tile_lds(it) - ring0);
+        const int f = hg;   // this wave's 16-row fragment
+        f32x4 sv[4];        // block scales of the lane's rows 16f + 4*g4 + j
+        float x[4];
+        float mx = NEG_INF;
+        if (active) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            sv[j] = *reinterpret_cast<const LDS_AS f32x4*>(tp + S::BODY_BYTES + (16 * f + 4 * g4 + j) * 16);
+          u32x4 kq[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            kq[i] = *reinterpret_cast<const LDS_AS u32x4*>(tp + kofs[f][i & 1] + (i >> 1) * S::RT * 128);
+          bf16x8 kr[2];
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
+            kr[kk] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[f][kk] + 4 * S::RT * 128);
+          f32x4 ab[4], ar[2];
+#pragma unroll
+          for (int blk = 0; blk < 4; ++blk) ab[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+          ar[0] = ar[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk) {
+              const int kk = 4 * blk + ks;
+              const u32x4 v = kq[2 * blk + (ks >> 1)];
+              const bf16x8 kb = (ks & 1) ? fp8x8_to_bf16(v[2], v[3]) : fp8x8_to_bf16(v[0], v[1]);
+              ab[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb[kk], ab[blk], 0, 0, 0);
+            }
+            if (ks < 2) ar[ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks], qb[16 + ks], ar[ks], 0, 0, 0);
+          }
+          f32x4 sc = ar[0] + ar[1];
+#pragma unroll
+          for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sc[j] += ab[blk][j] * sv[j][blk];
+          const int left = n_valid - tstart;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float v = sc[j] * a.scale_log2;
+            x[j] = (16 * f + 4 * g4 + j < left) ? v : NEG_INF;
+            mx = fmaxf(mx, x[j]);
+          }
+          mx = max_xor16_32(mx);
+        }
+        LDS_AS float* mex = (LDS_AS float*)(lds + S::MEX_OFF);
+        if (it == 0) {
+          // the pair's exponent reference (set once per row): the first tile's
+          // maximum over its 32 rows; both waves of a pair hold the same state
+          mex[wave * 64 + lane] = (m_run == NEG_INF) ? mx : m_run;
+          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          const float other = mex[(wave ^ 1) * 64 + lane];
+          if (m_run == NEG_INF) m_run = fmaxf(mx, other);
+        }
+        bf16x4 pb[4];   // P scaled by each 128-dim block's scale of the row
+        if (active) {
+          m_seen = fmaxf(m_seen, mx);
+          overflow |= (mx > m_run + REF_HEADROOM);
+          float psum = 0.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float pj = fast_exp2(x[j] - m_run);
+            psum += pj;
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk) pb[blk][j] = (__bf16)(pj * sv[j][blk]);
+          }
+          l_run += psum;
+#pragma unroll
+          for (int blk = 0; blk < 4; ++blk)
+            *(LDS_AS bf16x4*)(lds + S::PEX_OFF + ((rg * 4 + blk) * 64 + lane) * 16 + f * 8) = pb[blk];
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (active) {
+          // B operands of this wave's two blocks: rows 4*g4 + j (fragment 0), 16 + 4*g4 + j (fragment 1)
+          bf16x8 pall[2];
+#pragma unroll
+          for (int b2 = 0; b2 < 2; ++b2)
+            pall[b2] = *(const LDS_AS bf16x8*)(lds + S::PEX_OFF + ((rg * 4 + 2 * f + b2) * 64 + lane) * 16);
+          typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+          i32x2 vw[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            vw[i] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (LDS_AS i32x2*)(tp + tr8ofs[i & 7] + (2 * f + (i >> 3)) * S::RT * 128));
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            o[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16((uint32_t)vw[i][0], (uint32_t)vw[i][1]),
+                                                           pall[i >> 3], o[i], 0, 0, 0);
+        }
+      }
+    };
+
     // the compiler's wait for the query loads lands here, before any gather is in flight
 #pragma unroll
     for (int kk = 0; kk < 18; ++kk) asm volatile("" : : "v"(qb[kk]));
@@ -787,7 +896,8 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
             ++iss;
           }
         }
-        if (it < nt_rg) compute(it);
+        if constexpr (S::PAIR) compute_pair(it, it < nt_rg);
+        else if (it < nt_rg) compute(it);
       }
     }
     wait_vm<0>();
@@ -796,7 +906,15 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
   // rare: some tile exceeded the reference headroom -> recompute the row
   // (every wave of the work-group takes the same decision)
   if (!__syncthreads_or(overflow ? 1 : 0)) break;
-  m_run = m_seen;
+  if constexpr (S::PAIR) {
+    LDS_AS float* mex = (LDS_AS float*)(lds + S::MEX_OFF);
+    mex[wave * 64 + lane] = m_seen;
+    __syncthreads();
+    m_run = fmaxf(m_seen, mex[(wave ^ 1) * 64 + lane]);
+    __syncthreads();
+  } else {
+    m_run = m_seen;
+  }
   l_run = 0.f;
   overflow = false;
 #pragma unroll
@@ -818,6 +936,11 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
 #pragma unroll
       for (int hf = 0; hf < 4; ++hf)
         (reinterpret_cast<f32x4*>(smem) + (size_t)hf * 32 * 64)[(8 * hg + f) * 64 + lane] = o[4 * f + hf];
+  } else if constexpr (S::PAIR) {
+    // the row stream's 32 fragments, staged where its first wave's would be
+    f32x4* ost = reinterpret_cast<f32x4*>(smem) + (size_t)(rg * S::HG) * 32 * 64;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ost[(16 * hg + i) * 64 + lane] = o[i];
   } else {
     f32x4* ost = reinterpret_cast<f32x4*>(smem) + (size_t)wave * 32 * 64;
 #pragma unroll
@@ -838,7 +961,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
       for (int r = 0; r < S::NRG; ++r) {
         const int w = r * S::HG + hgi;
         const float fct = fast_exp2(stat[(w * 16 + nn) * 2] - M);
-        L += fct * stat[(w * 16 + nn) * 2 + 1];
+        L += fct * (stat[(w * 16 + nn) * 2 + 1] + (S::PAIR ? stat[((w + 1) * 16 + nn) * 2 + 1] : 0.f));
         // dims 8c..8c+7 = fragment c/2, lanes (2*(c&1) + {0,1})*16 + nn, j = 0..3
         const f32x4* ost = reinterpret_cast<const f32x4*>(smem) + (size_t)w * 32 * 64 + (c >> 1) * 64;
         const f32x4 v0 = ost[(2 * (c & 1) + 0) * 16 + nn];
@@ -953,13 +1076,14 @@ using V_H2_A = Shape<2, 2, 32, 2, 0>;
 using V_H2_B = Shape<2, 1, 32, 4, 0>;
 using V_H4_A = Shape<4, 1, 32, 4, 0, true, true>;
 using V_H4_B = Shape<4, 1, 32, 4, 0>;
-using F_H1_A = Shape<1, 2, 32, 3, 1>;
+using F_H1_A = Shape<2, 2, 32, 3, 1, false, false, true>;
+using F_H1_B = Shape<1, 2, 32, 3, 1>;
 using F_H2_A = Shape<2, 1, 32, 4, 1>;
 using F_H4_A = Shape<4, 1, 32, 7, 1>;
 
 template <class S>
 FwdShape shape_of() {
-  return FwdShape{S::HG, S::NRG, S::RT, S::NST, S::NTHR, S::LDS_BYTES};
+  return FwdShape{S::HEAD_GROUPS, S::NRG, S::RT, S::NST, S::NTHR, S::LDS_BYTES};
 }
 
 template <class S>
@@ -972,9 +1096,9 @@ hipError_t launch_one(const FwdArgs& a, int64_t grid, hipStream_t stream) {
 
 bool fwd_shape(int kv_format, int head_groups, int variant, FwdShape* shape) {
   if (kv_format == 1) {
-    if (variant != 0) return false;
+    if (variant != 0 && !(variant == 1 && head_groups == 1)) return false;
     switch (head_groups) {
-      case 1: *shape = shape_of<F_H1_A>(); return true;
+      case 1: *shape = variant == 1 ? shape_of<F_H1_B>() : shape_of<F_H1_A>(); return true;
       case 2: *shape = shape_of<F_H2_A>(); return true;
       case 4: *shape = shape_of<F_H4_A>(); return true;
       default: return false;
@@ -994,7 +1118,7 @@ hipError_t launch_fwd(const FwdArgs& a, int kv_format, int head_groups, int vari
                       hipStream_t stream) {
   if (kv_format == 1) {
     switch (head_groups) {
-      case 1: return launch_one<F_H1_A>(a, grid, stream);
+      case 1: return variant == 1 ? launch_one<F_H1_B>(a, grid, stream) : launch_one<F_H1_A>(a, grid, stream);
       case 2: return launch_one<F_H2_A>(a, grid, stream);
       case 4: return launch_one<F_H4_A>(a, grid, stream);
       default: return hipErrorInvalidValue;

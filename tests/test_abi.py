@@ -67,7 +67,8 @@ def test_zero_tokens_is_noop():
     (dict(max_blocks_per_seq=4, block_table_stride=3), B.SMLA_ERR_INVALID_ARG),
     (dict(kernel_variant=-1), B.SMLA_ERR_INVALID_ARG),
     (dict(kernel_variant=7), B.SMLA_ERR_UNSUPPORTED),
-    (dict(kernel_variant=1, kv_format="fp8"), B.SMLA_ERR_UNSUPPORTED),
+    (dict(kernel_variant=1, kv_format="fp8", num_heads=32), B.SMLA_ERR_UNSUPPORTED),
+    (dict(kernel_variant=2, kv_format="fp8"), B.SMLA_ERR_UNSUPPORTED),
     (dict(kernel_variant=2), B.SMLA_ERR_UNSUPPORTED),                 # h = 8: no third shape
     (dict(kernel_variant=2, num_heads=64), B.SMLA_ERR_UNSUPPORTED),
 ])
@@ -116,6 +117,12 @@ def test_plan_for_is_pure_and_splits_small_batches():
     assert B.plan(_params(num_heads=32), num_cus=256).head_groups == 2
     assert B.plan(_params(num_heads=64), num_cus=256).head_groups == 4
     assert B.plan(_params(num_heads=8, tiling="pad64"), num_cus=256).head_groups == 4
+    # fp8, h <= 16: one head group, two row streams of two waves each (the
+    # launch dispatches on the plan's head-group count)
+    pf = B.plan(_params(num_heads=8, kv_format="fp8", num_tokens=4096, topk=2048), num_cus=256)
+    assert pf.head_groups == 1 and pf.row_groups == 2 and pf.threads == 256
+    pf1 = B.plan(_params(num_heads=8, kv_format="fp8", kernel_variant=1), num_cus=256)
+    assert pf1.head_groups == 1 and pf1.threads == 128
     # grid is a multiple of 8 (XCD-aware mapping)
     assert B.plan(_params(num_tokens=1001, topk=64), num_cus=256).grid == 1008
 

@@ -322,7 +322,7 @@ def test_many_tokens_grid():
 
 # --------------------------------------------------------------------------- fp8 latent cache
 
-@pytest.mark.parametrize("h", [8, 16, 32, 64])
+@pytest.mark.parametrize("h", [8, 12, 16, 32, 64])
 def test_fp8_mini_heads(h):
     say("fp8 mini heads", h)
     c = G.make_mini(seed=51, num_heads=h, topk=300, kv_format="fp8")
@@ -340,6 +340,38 @@ def test_fp8_splits_and_slot_mode(splits):
     sidx = torch.from_numpy(slot_indices(c)).cuda()
     os_, ls = to_np(*run_gpu(dev, logical=False, idx_t=sidx, num_splits=splits))
     assert np.array_equal(out, os_) and np.array_equal(lse, ls)
+
+
+@pytest.mark.parametrize("h,variant", [(8, 1), (16, 1), (12, 1)])
+def test_fp8_alternative_shape(h, variant):
+    say("fp8 variant", h, variant)
+    c = G.make_mini(seed=54, num_heads=h, topk=300, kv_format="fp8")
+    out, lse = to_np(*run_gpu(Dev(c), variant=variant))
+    check(out, lse, *oracle(c), what="fp8 h=%d v%d" % (h, variant))
+
+
+@pytest.mark.parametrize("topk", [5, 40, 70])
+def test_fp8_short_lists(topk):
+    """One tile (the second row stream of a work-group idle), two tiles, and a
+    ragged third tile."""
+    say("fp8 short lists", topk)
+    c = G.make_mini(seed=55, num_heads=8, topk=topk, kv_format="fp8")
+    out, lse = to_np(*run_gpu(Dev(c)))
+    check(out, lse, *oracle(c), what="fp8 topk=%d" % topk)
+
+
+@pytest.mark.parametrize("splits", [1, 2])
+def test_fp8_large_score_spread_recomputes(splits):
+    """Queries scaled by 64 (exact in bf16) spread the scores of a row far
+    beyond the exponent headroom of its first tile: the recomputation with
+    the exact maximum must still match the oracle."""
+    say("fp8 score spread", splits)
+    c = G.make_mini(seed=56, num_heads=8, topk=300, kv_format="fp8")
+    qf = (c.q.astype(np.uint32) << 16).view(np.float32)
+    q = G.to_bf16_bits(qf * 64.0)
+    c2 = G.Case(**{**c.__dict__, "q": q})
+    out, lse = to_np(*run_gpu(Dev(c2), num_splits=splits))
+    check(out, lse, *oracle(c2), what="fp8 spread")
 
 
 def test_fp8_page_size_16_and_wide_index():
