@@ -781,9 +781,8 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
       };
       // scores of tile itq (K operands through a ring of KRING reads) with the
       // gathers of tile itd interleaved, one 128-B line per four MFMAs
-      auto scores = [&](int itq, int itd, f32x4* out) {
+      auto scores = [&](int itq, f32x4* out) {
         const LDS_AS uint8_t* tp = tptr(itq);
-        dma_prep(itd);   // its list entry is read before the ring starts
         // MFMA i is (fragment i & 1, k-step i >> 1); it accumulates into chain
         // (fragment, k-step mod 4), so each of the 8 chains is fed every 8th MFMA
         // and no MFMA waits for its predecessor's result
@@ -791,7 +790,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < KRING; ++i)
           kr[i] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[i & 1][(i >> 1) & 1] + (i >> 2) * S::RT * 128);
-        __builtin_amdgcn_sched_group_barrier(0x100, KRING + 1, 0);   // the list entry and the ring's first reads
+        __builtin_amdgcn_sched_group_barrier(0x100, KRING, 0);   // the ring's first reads
         f32x4 acc[2][4];
 #pragma unroll
         for (int f = 0; f < 2; ++f)
@@ -804,7 +803,6 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
           const int j = i + KRING;
           if (j < 36)
             kr[j] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[j & 1][(j >> 1) & 1] + (j >> 2) * S::RT * 128);
-          if ((i & 3) == 3) dma_line(i >> 2);
           // one MFMA, then its ring read
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           if (j < 36) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
@@ -824,15 +822,15 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
 
       if (nit > 0) {
 #pragma unroll
-        for (int st = 0; st < S::NST - 1; ++st) {
+        for (int st = 0; st < S::NST; ++st) {
           dma_prep(st);
 #pragma unroll
           for (int L = 0; L < 9; ++L) dma_line(L);
         }
-        wait_vm<(S::NST - 2) * S::PER>();
+        wait_vm<(S::NST - 1) * S::PER>();
         lds_barrier();
         f32x4 sc[2];
-        scores(0, S::NST - 1, sc);
+        scores(0, sc);
         bf16x8 vpre[8];
 #pragma unroll
         for (int f = 0; f < 8; ++f) vpre[f] = read_vt(0, f);
@@ -846,7 +844,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
           f32x4 scn[2];
           if (it + 1 < nit) {
             pb = softmax(it, sc);
-            scores(it + 1, it + S::NST, scn);
+            scores(it + 1, scn);
           } else {
             pb = softmax(it, sc);
             scn[0] = scn[1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -858,14 +856,19 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
 #pragma unroll
           for (int hf = 0; hf < 4; ++hf) pall[hf] = pex[hf * 64 + lane];
           // P.V of tile it over this wave's 8 output fragments x 4 head groups;
-          // each fragment's V^T registers are refilled from tile it+1 once used
+          // each fragment's V^T registers are refilled from tile it+1 once used;
+          // the gathers of tile it + NST (into tile it's slot, free since the
+          // last step) are issued under these MFMAs, one 128-B line per fragment
+          dma_prep(it + S::NST);
 #pragma unroll
           for (int f = 0; f < 8; ++f) {
 #pragma unroll
             for (int hf = 0; hf < 4; ++hf)
               o[4 * f + hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vpre[f], pall[hf], o[4 * f + hf], 0, 0, 0);
             vpre[f] = read_vt(it + 1, f);
+            dma_line(f);
           }
+          dma_line(8);
           sc[0] = scn[0];
           sc[1] = scn[1];
         }
