@@ -46,6 +46,7 @@ def parse():
     ap.add_argument("--workload", default="c2_decode")
     ap.add_argument("--splits", type=int, default=0, help="0 = automatic plan")
     ap.add_argument("--variant", type=int, default=0)
+    ap.add_argument("--gather-order", default="auto", choices=["auto", "list", "slot"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--cold-launches", type=int, default=50)
@@ -155,7 +156,7 @@ def main():
     lse = torch.empty((T, h), dtype=torch.float32, device="cuda")
     p = B.params_for(q, dev.kv, dev.idx, out, lse, topk=case.topk, scale=case.scale, page_size=case.page_size,
                      kv_format=case.kv_format, block_table=dev.bt, token_seq=dev.ts, tiling=tiling,
-                     num_splits=args.splits, kernel_variant=args.variant)
+                     num_splits=args.splits, kernel_variant=args.variant, gather_order=args.gather_order)
     pl = B.plan(p)
     ws = B.workspace_for(p, "cuda")
     pws = torch.empty(max(16, pl.partials_bytes), dtype=torch.uint8, device="cuda")
@@ -293,6 +294,7 @@ def main():
         "config": {"workload": wl_name, "num_tokens": T, "num_heads": h, "topk": case.topk,
                    "kv_format": case.kv_format, "page_size": case.page_size, "tiling": tiling,
                    "num_splits": pl.num_splits, "kernel_variant": args.variant,
+                   "gather_order": {1: "list", 2: "slot"}[pl.gather_order],
                    "grid": pl.grid, "threads": pl.threads},
         "gathered_GBps_per_step": round(gathered / (ms_per_step * 1e-3) / 1e9, 1),
         "mfma_frac_per_step": round(flops / (ms_per_step * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 5),

@@ -91,6 +91,16 @@ extern "C" {
 #define SMLA_TILING_NATIVE 1
 #define SMLA_TILING_PAD64 2
 
+/* Gather order (smla_params.gather_order).  LIST follows the index list;
+ * SLOT groups each row's entries (stably) into 16 ranges of physical cache
+ * row, so that the rows computed at the same time on one XCD read nearby
+ * cache rows and share its L2.  AUTO picks SLOT for unsplit bf16 batches of
+ * at least 1024 query rows (prefill-sized; rows of one sequence overlap in
+ * their history) and LIST otherwise. */
+#define SMLA_GATHER_AUTO 0
+#define SMLA_GATHER_LIST 1
+#define SMLA_GATHER_SLOT 2
+
 #define SMLA_D_QK 576
 #define SMLA_D_V 512
 #define SMLA_MAX_HEADS 64
@@ -120,6 +130,9 @@ typedef struct smla_params {
   int32_t kernel_variant;      /* 0 = default pipeline shape; 1 = alternative shape   */
                                /* (bf16 only; others -> SMLA_ERR_UNSUPPORTED); a      */
                                /* tuning knob, see smla_plan; same results to tol.    */
+  int32_t gather_order;        /* SMLA_GATHER_*: order in which a row's listed cache  */
+                               /* rows are gathered (the result is the same set sum;  */
+                               /* fp32 summation order, hence rounding, follows it)   */
 } smla_params;
 
 /* Read-only description of how a call with these parameters is executed. */
@@ -136,6 +149,7 @@ typedef struct smla_plan {
   int64_t partials_bytes;      /* workspace sparse_mla_fwd_partials writes            */
   int32_t lds_bytes;           /* LDS per work-group                                  */
   int32_t num_cus;             /* compute units assumed by the plan                   */
+  int32_t gather_order;        /* resolved SMLA_GATHER_LIST or SMLA_GATHER_SLOT        */
 } smla_plan;
 
 /* Bytes of workspace sparse_mla_fwd needs for calls described by *p.

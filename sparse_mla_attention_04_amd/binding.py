@@ -25,6 +25,7 @@ SMLA_ERR_HIP = 4
 KV_FORMATS = {"bf16": 0, "fp8": 1}
 INDEX_MODES = {"slot": 0, "logical": 1}
 TILINGS = {"auto": 0, "native": 1, "pad64": 2}
+GATHER_ORDERS = {"auto": 0, "list": 1, "slot": 2}
 D_QK, D_V = 576, 512
 
 EXPORTS = ("sparse_mla_workspace_size", "sparse_mla_plan", "sparse_mla_plan_for",
@@ -45,6 +46,7 @@ class Params(ctypes.Structure):
         ("block_table_stride", ctypes.c_int64),
         ("softmax_scale", ctypes.c_float), ("tiling", ctypes.c_int32),
         ("num_splits", ctypes.c_int32), ("kernel_variant", ctypes.c_int32),
+        ("gather_order", ctypes.c_int32),
     ]
 
 
@@ -57,6 +59,7 @@ class Plan(ctypes.Structure):
         ("workspace_bytes", ctypes.c_int64), ("partials_bytes", ctypes.c_int64),
         ("lds_bytes", ctypes.c_int32),
         ("num_cus", ctypes.c_int32),
+        ("gather_order", ctypes.c_int32),
     ]
 
     def as_dict(self):
@@ -110,6 +113,7 @@ def make_params(*, num_tokens: int, num_heads: int, topk: int, idx_stride: Optio
                 index_mode: str = "logical", num_seqs: int = 0, max_blocks_per_seq: int = 0,
                 block_table_stride: Optional[int] = None, scale: float = 1.0 / 24.0,
                 tiling: str = "auto", num_splits: int = 0, kernel_variant: int = 0,
+                gather_order: str = "auto",
                 q_strides=None, out_strides=None, lse_stride: Optional[int] = None) -> Params:
     p = Params()
     p.num_tokens, p.num_heads, p.topk, p.page_size = num_tokens, num_heads, topk, page_size
@@ -128,6 +132,7 @@ def make_params(*, num_tokens: int, num_heads: int, topk: int, idx_stride: Optio
     p.tiling = TILINGS[tiling]
     p.num_splits = num_splits
     p.kernel_variant = kernel_variant
+    p.gather_order = GATHER_ORDERS[gather_order]
     return p
 
 
@@ -154,7 +159,7 @@ def _ptr(t) -> Optional[int]:
 
 def params_for(q, kv, topk_idx, out, lse, *, topk: int, scale: float, page_size: int = 64,
                kv_format: str = "bf16", block_table=None, token_seq=None, tiling: str = "auto",
-               num_splits: int = 0, kernel_variant: int = 0) -> Params:
+               num_splits: int = 0, kernel_variant: int = 0, gather_order: str = "auto") -> Params:
     """smla_params from tensors: q bf16 [T, h, 576] (last dim contiguous), kv the
     cache pool (bf16 [pages, P, 576] or uint8 [pages, P * 656]), topk_idx int32
     [T, >= topk], out bf16 [T, h, 512], lse fp32 [T, h]."""
@@ -169,7 +174,7 @@ def params_for(q, kv, topk_idx, out, lse, *, topk: int, scale: float, page_size:
         max_blocks_per_seq=int(block_table.shape[1]) if logical else 0,
         block_table_stride=int(block_table.stride(0)) if logical else 0,
         scale=scale, tiling=tiling, num_splits=num_splits, kernel_variant=kernel_variant,
-        q_strides=(int(q.stride(0)), int(q.stride(1))),
+        gather_order=gather_order, q_strides=(int(q.stride(0)), int(q.stride(1))),
         out_strides=(int(out.stride(0)), int(out.stride(1))),
         lse_stride=int(lse.stride(0)))
 

@@ -87,7 +87,7 @@ struct Shape {
   // exponent reference.
   static constexpr bool PAIR = PAIR_;
   static constexpr int HEAD_GROUPS = PAIR ? 1 : HG;   // 16-head groups the shape covers
-  static constexpr int PEX_OFF = CNT_OFF + 64;
+  static constexpr int PEX_OFF = CNT_OFF + 512;   // per-wave counts: NW x 8 words
   static constexpr int PEX_BYTES = DSPLIT ? 4 * 64 * 16 : PAIR ? NRG * 4 * 64 * 16 : 0;
   static constexpr int MEX_OFF = PEX_OFF + PEX_BYTES;
   static constexpr int STAT_OFF = MEX_OFF + (PAIR ? NW * 64 * 4 : 0);
@@ -212,9 +212,22 @@ __device__ __forceinline__ int translate(const FwdArgs& a, int j, int seq_ok, in
   return (page << a.page_shift) | (j & ((1 << a.page_shift) - 1));
 }
 
-// Translate a thread's EPT raw index entries, compact the surviving rows in
-// order into list[] (a wave-level prefix sum, then the waves' offsets), and
-// return the chunk's count.  Two work-group barriers.
+// 16-bit field g of a packed array (two fields per word), g a runtime value
+__device__ __forceinline__ uint32_t field16(const uint32_t (&w)[8], int g) {
+  uint32_t v = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v = ((g >> 1) == k) ? w[k] : v;
+  return (v >> ((g & 1) * 16)) & 0xffffu;
+}
+
+// Translate a thread's EPT raw index entries and compact the surviving rows
+// into list[]; returns the chunk's count.  Two work-group barriers.
+//   list order (a.bucket_shift < 0): survivors keep the index list's order
+//     (a wave prefix sum, then the waves' offsets);
+//   slot order: a stable counting sort of the survivors into 16 groups of
+//     physical row (slot >> bucket_shift), list order inside a group, so the
+//     rows that run together on one XCD read nearby cache rows.  Counts are
+//     packed two groups per 32-bit word (each at most 2048 per pass).
 template <int NW, int EPT>
 __device__ __forceinline__ int compact_chunk(const FwdArgs& a, const int (&raw)[EPT], int seq_ok, int64_t bt_row,
                                              int* list, int* wcnt, int wave, int lane) {
@@ -226,28 +239,92 @@ __device__ __forceinline__ int compact_chunk(const FwdArgs& a, const int (&raw)[
     sl[i] = s;
     cnt += (s >= 0);
   }
-  int incl = cnt;
+  if (a.bucket_shift < 0) {
+    int incl = cnt;
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int v = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += v;
-  }
-  if (lane == 63) wcnt[wave] = incl;
-  __syncthreads();
-  int base = 0, n_valid = 0;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += v;
+    }
+    if (lane == 63) wcnt[wave] = incl;
+    __syncthreads();
+    int base = 0, n_valid = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const int c = wcnt[w];
-    base += (w < wave) ? c : 0;
-    n_valid += c;
+    for (int w = 0; w < NW; ++w) {
+      const int c = wcnt[w];
+      base += (w < wave) ? c : 0;
+      n_valid += c;
+    }
+    int pos = base + incl - cnt;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      if (sl[i] >= 0) { list[pos] = sl[i]; ++pos; }
+    }
+    __syncthreads();
+    return n_valid;
   }
-  int pos = base + incl - cnt;
+  int grp[EPT];
+  uint32_t own[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) own[k] = 0;
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
-    if (sl[i] >= 0) { list[pos] = sl[i]; ++pos; }
+    const int g = (sl[i] >= 0) ? (sl[i] >> a.bucket_shift) : -1;
+    grp[i] = g;
+    const uint32_t one = (g >= 0) ? (1u << ((g & 1) * 16)) : 0u;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) own[k] += ((g >> 1) == k) ? one : 0u;
+  }
+  uint32_t inc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) inc[k] = own[k];
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t v = __shfl_up(inc[k], d, 64);
+      if (lane >= d) inc[k] += v;
+    }
+  }
+  uint32_t* wc = reinterpret_cast<uint32_t*>(wcnt);
+  if (lane == 63) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) wc[wave * 8 + k] = inc[k];
   }
   __syncthreads();
-  return n_valid;
+  uint32_t before[8], total[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) before[k] = total[k] = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t v = wc[w * 8 + k];
+      total[k] += v;
+      before[k] += (w < wave) ? v : 0u;
+    }
+  // base of each group for this thread: group start + earlier waves + earlier lanes
+  uint32_t base[8];
+  uint32_t running = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t t0 = total[k] & 0xffffu, t1 = total[k] >> 16;
+    const uint32_t start = running | ((running + t0) << 16);
+    running += t0 + t1;
+    base[k] = start + before[k] + (inc[k] - own[k]);
+  }
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int g = grp[i];
+    if (g >= 0) {
+      list[field16(base, g)] = sl[i];
+      const uint32_t one = 1u << ((g & 1) * 16);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) base[k] += ((g >> 1) == k) ? one : 0u;
+    }
+  }
+  __syncthreads();
+  return (int)running;
 }
 
 template <class S>

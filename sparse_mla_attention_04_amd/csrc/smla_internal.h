@@ -25,6 +25,7 @@ struct FwdArgs {
   int32_t grid_per_xcd;       // launched work-groups / 8
   int32_t write_partials;     // 1: write fp32 partials to ws_out / ws_lse instead of out / lse
   float scale_log2;           // softmax_scale * log2(e)
+  int32_t bucket_shift;       // >= 0: gather each row's entries grouped by (slot >> shift), 16 groups; -1: list order
 };
 
 struct CombineArgs {

@@ -42,7 +42,7 @@ def slot_indices(case, idx=None) -> np.ndarray:
 
 
 def run_gpu(dev: Dev, *, heads=None, logical=True, idx_t=None, tiling="auto", num_splits=0, variant=0,
-            topk=None, out=None, lse=None, workspace=None):
+            topk=None, out=None, lse=None, workspace=None, gather_order="auto"):
     """sparse_mla_fwd through the binding; returns device out / lse."""
     c = dev.case
     h = c.num_heads if heads is None else heads
@@ -56,7 +56,7 @@ def run_gpu(dev: Dev, *, heads=None, logical=True, idx_t=None, tiling="auto", nu
     p = B.params_for(q, dev.kv, idx, out, lse, topk=c.topk if topk is None else topk, scale=c.scale,
                      page_size=c.page_size, kv_format=c.kv_format,
                      block_table=dev.bt if logical else None, token_seq=dev.ts if logical else None,
-                     tiling=tiling, num_splits=num_splits, kernel_variant=variant)
+                     tiling=tiling, num_splits=num_splits, kernel_variant=variant, gather_order=gather_order)
     if workspace is None:
         workspace = B.workspace_for(p, dev.q.device)
     B.fwd(q, dev.kv, idx, out, lse, topk=p.topk, scale=c.scale, workspace=workspace,

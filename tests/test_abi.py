@@ -77,6 +77,27 @@ def test_bad_params_rejected(kw, code):
     assert B.workspace_size(_params(**kw)) == 0
 
 
+def test_bad_gather_order_rejected():
+    for v in (-1, 3):
+        p = _params()
+        p.gather_order = v
+        assert _fwd(p) == B.SMLA_ERR_INVALID_ARG
+        assert B.workspace_size(p) == 0
+
+
+def test_gather_order_resolution():
+    # prefill-sized unsplit batches gather in slot order, decode-sized split ones in list order
+    assert B.plan(_params(num_tokens=4096, topk=2048), num_cus=256).gather_order == B.GATHER_ORDERS["slot"]
+    assert B.plan(_params(num_tokens=32, topk=2048), num_cus=256).gather_order == B.GATHER_ORDERS["list"]
+    assert B.plan(_params(num_tokens=1000, topk=2048), num_cus=256).gather_order == B.GATHER_ORDERS["list"]
+    assert B.plan(_params(num_tokens=4096, topk=2048, kv_format="fp8"), num_cus=256).gather_order == \
+        B.GATHER_ORDERS["list"]
+    assert B.plan(_params(num_tokens=32, topk=2048, gather_order="slot"), num_cus=256).gather_order == \
+        B.GATHER_ORDERS["slot"]
+    assert B.plan(_params(num_tokens=4096, topk=2048, gather_order="list"), num_cus=256).gather_order == \
+        B.GATHER_ORDERS["list"]
+
+
 def test_bad_pointers_rejected():
     p = _params()
     assert _fwd(p, q=None) == B.SMLA_ERR_INVALID_ARG

@@ -427,3 +427,39 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), "replay %d differs" % rep
     check(*to_np(out, lse), *oracle(c), what="graph replay")
+
+
+# --------------------------------------------------------------------------- slot-ordered gathers
+
+@pytest.mark.parametrize("h,kv_format,splits,topk", [(8, "bf16", 1, 300), (16, "bf16", 3, 300), (64, "bf16", 1, 300),
+                                                     (32, "bf16", 1, 300), (8, "fp8", 1, 333), (8, "fp8", 2, 333),
+                                                     (8, "bf16", 1, 5000)])
+def test_slot_order_matches_oracle(h, kv_format, splits, topk):
+    """Gathers grouped by physical row (stable counting sort in the kernel)
+    give the oracle's result; list order and slot order agree to the split
+    tolerance; SLOT and LOGICAL indices stay bit-identical under slot order."""
+    say("slot order", h, kv_format, splits, topk)
+    c = G.make_mini(seed=61, num_heads=h, topk=topk, kv_format=kv_format, drop_frac=0.2)
+    dev = Dev(c)
+    out, lse = to_np(*run_gpu(dev, num_splits=splits, gather_order="slot"))
+    check(out, lse, *oracle(c), what="slot order h=%d %s" % (h, kv_format))
+    o2, l2 = to_np(*run_gpu(dev, num_splits=splits, gather_order="list"))
+    fin = np.isfinite(l2)
+    assert np.abs(out - o2).max() <= 2e-2 and np.abs(lse[fin] - l2[fin]).max() <= SPLIT_ATOL
+    sidx = torch.from_numpy(slot_indices(c)).cuda()
+    os_, ls = to_np(*run_gpu(dev, logical=False, idx_t=sidx, num_splits=splits, gather_order="slot"))
+    assert np.array_equal(out, os_) and np.array_equal(lse, ls)
+
+
+def test_auto_gather_order_on_prefill_batch():
+    """c3 at h=8 runs in slot order by default (4096 unsplit rows)."""
+    say("auto gather order c3")
+    c = G.make_config("c3_sweep").with_heads(8)
+    dev = Dev(c)
+    p = B.params_for(dev.q, dev.kv, dev.idx, torch.empty((c.num_tokens, 8, 512), dtype=torch.bfloat16, device="cuda"),
+                     torch.empty((c.num_tokens, 8), dtype=torch.float32, device="cuda"), topk=c.topk, scale=c.scale,
+                     block_table=dev.bt, token_seq=dev.ts)
+    assert B.plan(p).gather_order == B.GATHER_ORDERS["slot"]
+    out, lse = to_np(*run_gpu(dev))
+    rows = np.unique(np.r_[np.arange(0, c.num_tokens, 97), c.num_tokens - 1])
+    check(out[rows], lse[rows], *oracle(c, rows=rows), what="c3 h8 slot order")
