@@ -908,6 +908,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         lds_barrier();
         f32x4 sc[2];
         scores(0, sc);
+        bf16x8 pb = softmax(0, sc);   // P of tile 0
         bf16x8 vpre[8];
 #pragma unroll
         for (int f = 0; f < 8; ++f) vpre[f] = read_vt(0, f);
@@ -917,16 +918,13 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
           // every wave's reads of tile it (its V^T operands) have completed
           // before any gather refills that slot
           asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-          bf16x8 pb;
           f32x4 scn[2];
           if (it + 1 < nit) {
-            pb = softmax(it, sc);
             scores(it + 1, scn);
           } else {
-            pb = softmax(it, sc);
             scn[0] = scn[1] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
-          // publish this head group's P, take all four
+          // publish this head group's P of tile it, take all four
           pex[hg * 64 + lane] = pb;
           asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
           bf16x8 pall[4];
@@ -935,8 +933,10 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
           // P.V of tile it over this wave's 8 output fragments x 4 head groups;
           // each fragment's V^T registers are refilled from tile it+1 once used;
           // the gathers of tile it + NST (into tile it's slot, free since the
-          // last step) are issued under these MFMAs, one 128-B line per fragment
+          // last step) and the softmax of tile it+1 run under these MFMAs
+          // (past the list the softmax sees only masked rows: no effect)
           dma_prep(it + S::NST);
+          pb = softmax(it + 1, scn);
 #pragma unroll
           for (int f = 0; f < 8; ++f) {
 #pragma unroll
@@ -946,8 +946,6 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
             dma_line(f);
           }
           dma_line(8);
-          sc[0] = scn[0];
-          sc[1] = scn[1];
         }
       }
     } else {
