@@ -128,8 +128,9 @@ typedef struct smla_params {
   int32_t tiling;              /* SMLA_TILING_*                                       */
   int32_t num_splits;          /* 0 = automatic; n >= 1 forces n KV splits per row    */
   int32_t kernel_variant;      /* 0 = default pipeline shape; 1 = alternative shape   */
-                               /* (bf16 only; others -> SMLA_ERR_UNSUPPORTED); a      */
-                               /* tuning knob, see smla_plan; same results to tol.    */
+                               /* (bf16 any h; fp8 h <= 16); anything else ->         */
+                               /* SMLA_ERR_UNSUPPORTED.  A tuning knob, see smla_plan;*/
+                               /* same results to tolerance.                          */
   int32_t gather_order;        /* SMLA_GATHER_*: order in which a row's listed cache  */
                                /* rows are gathered (the result is the same set sum;  */
                                /* fp32 summation order, hence rounding, follows it)   */
@@ -138,7 +139,8 @@ typedef struct smla_params {
 /* Read-only description of how a call with these parameters is executed. */
 typedef struct smla_plan {
   int32_t head_groups;         /* 16-head groups the kernel runs (1, 2 or 4)          */
-  int32_t row_groups;          /* waves per work-group that split the KV rows         */
+  int32_t row_groups;          /* independent row streams (tile sequences) per        */
+                               /* work-group                                          */
   int32_t tile_rows;           /* cache rows per pipeline stage                       */
   int32_t stages;              /* pipeline depth (tiles in LDS per row group)         */
   int32_t num_splits;          /* KV splits per query row (1 = unsplit)               */
