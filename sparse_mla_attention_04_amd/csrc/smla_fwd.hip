@@ -53,7 +53,7 @@ constexpr float LN2 = 0.69314718055994530942f;
 constexpr float REF_HEADROOM = 64.0f;   // p = 2^(x - ref) may reach 2^64 before a second pass is forced
 
 template <int HG_, int NRG_, int RT_, int NST_, int FMT_, bool DSPLIT_ = false, bool PIPE_ = false,
-          bool PAIR_ = false>
+          bool PAIR_ = false, bool RSPLIT_ = false>
 struct Shape {
   static constexpr int HG = HG_;            // 16-head groups (waves per row group)
   static constexpr int NRG = NRG_;          // row groups (independent KV row streams)
@@ -86,12 +86,24 @@ struct Shape {
   // P of the 4 dim blocks being exchanged through LDS.  The pair shares one
   // exponent reference.
   static constexpr bool PAIR = PAIR_;
+  // RSPLIT (with PIPE): wave w forms the scores and softmax of tile rows
+  // 16(w & 1) .. +15 for the 32 heads 32(w >> 1) .. +31, so every K operand read
+  // from LDS feeds two MFMAs; the two waves holding one head's row halves share
+  // its exponent reference and add their row sums at the end.
+  static constexpr bool RSPLIT = RSPLIT_;
+  static constexpr int NE = RSPLIT ? 2 : 1;            // 16-head groups in a wave's scores
   static constexpr int HEAD_GROUPS = PAIR ? 1 : HG;   // 16-head groups the shape covers
-  static constexpr int PEX_OFF = CNT_OFF + 512;   // per-wave counts: NW x 8 words
-  static constexpr int PEX_BYTES = DSPLIT ? 4 * 64 * 16 : PAIR ? NRG * 4 * 64 * 16 : 0;
+  // per-wave counts (NW x 8 words) at CNT_OFF.  The pipelined shapes keep the
+  // counts (compaction only), the P exchange (tile loop only) and the
+  // statistics (epilogue only) in one region; P is double-buffered there.
+  static constexpr int STAT_BYTES = NW * 16 * 2 * 4 * NE;
+  static constexpr int PEX_OFF = PIPE ? CNT_OFF : CNT_OFF + 512;
+  static constexpr int PEX_BYTES = DSPLIT ? 2 * 4 * 64 * 16 : PAIR ? NRG * 4 * 64 * 16 : 0;
   static constexpr int MEX_OFF = PEX_OFF + PEX_BYTES;
-  static constexpr int STAT_OFF = MEX_OFF + (PAIR ? NW * 64 * 4 : 0);
-  static constexpr int LDS_BYTES = STAT_OFF + NW * 16 * 2 * 4;
+  static constexpr int STAT_OFF = PIPE ? CNT_OFF : MEX_OFF + (PAIR ? NW * 64 * 4 : 0);
+  static constexpr int LDS_BYTES =
+      PIPE ? CNT_OFF + (PEX_BYTES > STAT_BYTES ? (PEX_BYTES > 512 ? PEX_BYTES : 512) : (STAT_BYTES > 512 ? STAT_BYTES : 512))
+           : STAT_OFF + STAT_BYTES;
   static constexpr int EPT = LIST_CAP / NTHR;   // index entries per thread per pass
   static constexpr bool SYNC = HG > 1;          // waves share tiles -> barrier per tile
   static_assert(RT == 16 || RT == 32, "tile rows");
@@ -99,12 +111,14 @@ struct Shape {
   static_assert(NRH % HG == 0, "DMA groups must split evenly over the waves of a row group");
   static_assert((NST - 1) * PER <= 63, "vmcnt holds at most 63 outstanding loads");
   static_assert(NW * 32 * 64 * 16 <= STAT_OFF, "epilogue staging must fit below the statistics");
+  static_assert(NW * 8 * 4 <= 512, "compaction counts");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(LIST_CAP % NTHR == 0, "compaction split");
   static_assert(!DSPLIT || (HG == 4 && NRG == 1 && RT == 32 && !FP8), "output-dim split layout");
   static_assert(!PIPE || (DSPLIT && NST >= 3 && PER == 9), "pipelined variant layout");
   static_assert(!DSPLIT || PIPE, "the output-dim split runs in the pipelined schedule");
   static_assert(!PAIR || (FP8 && HG == 2 && RT == 32 && !DSPLIT), "row/dim-split pair layout");
+  static_assert(!RSPLIT || PIPE, "the row-half score split runs in the pipelined schedule");
 };
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -367,6 +381,14 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
       vofs[f][p] = (uint32_t)(rv * 8 + ((2 * p + (cq >> 1)) ^ swv)) * 16u + (uint32_t)(cq & 1) * 8u;
   }
 
+  // RSPLIT: K operand of this wave's 16 tile rows 16*(wave & 1) + n, chunk 4p + g4
+  uint32_t krs[2];
+  {
+    const int r = 16 * (wave & 1) + n;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) krs[p] = (uint32_t)(r * 8 + ((4 * p + g4) ^ swz<S::FP8>(r))) * 16u;
+  }
+
   // fp8 rows: 40 chunks of 16 B ([512 codes | 64 bf16 rope]) laid out like the bf16 tile
   uint32_t tr8ofs[S::FP8 ? 8 : 1];         // transposing fp8 read: row kmap(g4, n>>1), 8 B at dims 16f + 8*(n&1)
   if constexpr (S::FP8) {
@@ -380,8 +402,15 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
   f32x4 o[32];
 #pragma unroll
   for (int f = 0; f < 32; ++f) o[f] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = NEG_INF, l_run = 0.f;   // exponent reference and row sum (per head lane)
-  float m_seen = NEG_INF;                 // true running maximum
+  // per 16-head group of the wave's scores (lane n: head n of the group)
+  float m_run[S::NE], l_run[S::NE];       // exponent reference and row sum
+  float m_seen[S::NE];                    // true running maximum
+#pragma unroll
+  for (int e = 0; e < S::NE; ++e) {
+    m_run[e] = NEG_INF;
+    l_run[e] = 0.f;
+    m_seen[e] = NEG_INF;
+  }
   bool overflow = false;
 
   // ---- index range of this split
@@ -403,9 +432,10 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
 
   // ---- queries of this wave's 16 heads, in the MFMA B-operand layout:
   //      lane (g4, n) holds head hg*16+n, dims 32*kk + 8*g4 .. +7
-  bf16x8 qb[18];
-  {
-    const int head = (S::PAIR ? 0 : hg) * 16 + n;
+  bf16x8 qb[18 * S::NE];   // RSPLIT: group e's k-step kk at qb[18e + kk]
+#pragma unroll
+  for (int e = 0; e < S::NE; ++e) {
+    const int head = (S::RSPLIT ? 32 * (wave >> 1) + 16 * e : (S::PAIR ? 0 : hg) * 16) + n;
     if (head < a.h) {
       const uint16_t* qp = a.q + (int64_t)t * a.q_st + (int64_t)head * a.q_sh + 8 * g4;
 #pragma unroll
@@ -417,11 +447,11 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         const int off = (S::FP8 && kk < 16)
                             ? 128 * (kk >> 2) + 64 * ((kk & 3) >> 1) + 8 * g4 + 8 * (kk & 1)
                             : 32 * kk;
-        qb[kk] = *reinterpret_cast<const bf16x8*>(qp + off);
+        qb[18 * e + kk] = *reinterpret_cast<const bf16x8*>(qp + off);
       }
     } else {
 #pragma unroll
-      for (int kk = 0; kk < 18; ++kk) qb[kk] = bf16x8{};
+      for (int kk = 0; kk < 18; ++kk) qb[18 * e + kk] = bf16x8{};
     }
   }
 
@@ -587,19 +617,19 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
       // the accumulators never need rescaling.  A tile that exceeds the
       // reference by more than the headroom flags the work-group, which then
       // recomputes the row once with its true maximum as the reference.
-      m_seen = fmaxf(m_seen, mx);
-      if (m_run == NEG_INF) m_run = mx;
-      overflow |= (mx > m_run + REF_HEADROOM);
+      m_seen[0] = fmaxf(m_seen[0], mx);
+      if (m_run[0] == NEG_INF) m_run[0] = mx;
+      overflow |= (mx > m_run[0] + REF_HEADROOM);
       float psum = 0.f;
       float pv[S::NF][4];
 #pragma unroll
       for (int f = 0; f < S::NF; ++f)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          pv[f][j] = fast_exp2(x[f][j] - m_run);
+          pv[f][j] = fast_exp2(x[f][j] - m_run[0]);
           psum += pv[f][j];
         }
-      l_run += psum;
+      l_run[0] += psum;
       // P.V
       // V^T operands are read in groups of 8 output fragments, the next
       // group's transposing reads in flight while the current group's MFMAs run
@@ -741,24 +771,24 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         if (it == 0) {
           // the pair's exponent reference (set once per row): the first tile's
           // maximum over its 32 rows; both waves of a pair hold the same state
-          mex[wave * 64 + lane] = (m_run == NEG_INF) ? mx : m_run;
+          mex[wave * 64 + lane] = (m_run[0] == NEG_INF) ? mx : m_run[0];
           asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
           const float other = mex[(wave ^ 1) * 64 + lane];
-          if (m_run == NEG_INF) m_run = fmaxf(mx, other);
+          if (m_run[0] == NEG_INF) m_run[0] = fmaxf(mx, other);
         }
         bf16x4 pb[4];   // P scaled by each 128-dim block's scale of the row
         if (active) {
-          m_seen = fmaxf(m_seen, mx);
-          overflow |= (mx > m_run + REF_HEADROOM);
+          m_seen[0] = fmaxf(m_seen[0], mx);
+          overflow |= (mx > m_run[0] + REF_HEADROOM);
           float psum = 0.f;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float pj = fast_exp2(x[j] - m_run);
+            const float pj = fast_exp2(x[j] - m_run[0]);
             psum += pj;
 #pragma unroll
             for (int blk = 0; blk < 4; ++blk) pb[blk][j] = (__bf16)(pj * sv[j][blk]);
           }
-          l_run += psum;
+          l_run[0] += psum;
 #pragma unroll
           for (int blk = 0; blk < 4; ++blk)
             *(LDS_AS bf16x4*)(lds + S::PEX_OFF + ((rg * 4 + blk) * 64 + lane) * 16 + f * 8) = pb[blk];
@@ -786,7 +816,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
 
     // the compiler's wait for the query loads lands here, before any gather is in flight
 #pragma unroll
-    for (int kk = 0; kk < 18; ++kk) asm volatile("" : : "v"(qb[kk]));
+    for (int kk = 0; kk < 18 * S::NE; ++kk) asm volatile("" : : "v"(qb[kk]));
 
     if constexpr (S::PIPE) {
       // ---- software-pipelined schedule (one tile stream, four waves):
@@ -825,41 +855,93 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         }
       };
       auto tptr = [&](int it) { return lds + (tile_lds(it) - ring0); };
-      // online softmax of one tile (base 2, fixed exponent reference); the
-      // lane owns head n and rows 16f + 4*g4 + j; returns P in the B-operand layout
-      auto softmax = [&](int it, const f32x4* scv) -> bf16x8 {
+      // online softmax of one tile (base 2, fixed exponent reference).  The
+      // lane owns head n of a 16-head group and rows 4*g4 + j of a 16-row
+      // fragment: scv[q] is fragment q (rows 16q + ..) of the wave's group, or
+      // with RSPLIT head group q of the wave's rows 16*(wave & 1) + ..; P comes
+      // back as pb[4q + j].  With RSPLIT, `first` (work-group uniform) sets the
+      // exponent reference of each head from the tile's maximum over both
+      // row halves, exchanged with the partner wave through LDS.
+      auto softmax = [&](int it, const f32x4* scv, bool first) -> bf16x8 {
         const int left = n_valid - it * S::RT;
         float x[2][4];
-        float mx = NEG_INF;
+        float mx[2] = {NEG_INF, NEG_INF};
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
+        for (int q = 0; q < 2; ++q)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float v = scv[f][j] * a.scale_log2;
-            x[f][j] = (16 * f + 4 * g4 + j < left) ? v : NEG_INF;
-            mx = fmaxf(mx, x[f][j]);
+            const int row = (S::RSPLIT ? 16 * (wave & 1) : 16 * q) + 4 * g4 + j;
+            const float v = scv[q][j] * a.scale_log2;
+            x[q][j] = (row < left) ? v : NEG_INF;
+            mx[S::RSPLIT ? q : 0] = fmaxf(mx[S::RSPLIT ? q : 0], x[q][j]);
           }
-        mx = max_xor16_32(mx);
-        m_seen = fmaxf(m_seen, mx);
-        if (m_run == NEG_INF) m_run = mx;
-        overflow |= (mx > m_run + REF_HEADROOM);
+#pragma unroll
+        for (int e = 0; e < S::NE; ++e) mx[e] = max_xor16_32(mx[e]);
+        if constexpr (S::RSPLIT) {
+          if (first) {
+            // in exchange buffer 1: buffer 0 receives P of this tile right after
+            LDS_AS float* mex = (LDS_AS float*)(lds + S::PEX_OFF + 4096);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) mex[(wave * 2 + e) * 64 + lane] = (m_run[e] == NEG_INF) ? mx[e] : m_run[e];
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const float other = mex[((wave ^ 1) * 2 + e) * 64 + lane];
+              if (m_run[e] == NEG_INF) m_run[e] = fmaxf(mx[e], other);
+            }
+          }
+        } else {
+          if (m_run[0] == NEG_INF) m_run[0] = mx[0];
+        }
+#pragma unroll
+        for (int e = 0; e < S::NE; ++e) {
+          m_seen[e] = fmaxf(m_seen[e], mx[e]);
+          overflow |= (mx[e] > m_run[e] + REF_HEADROOM);
+        }
         bf16x8 pb;
-        float psum = 0.f;
+        float psum[2] = {0.f, 0.f};
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
+        for (int q = 0; q < 2; ++q)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float pj = fast_exp2(x[f][j] - m_run);
-            psum += pj;
-            pb[4 * f + j] = (__bf16)pj;
+            const float pj = fast_exp2(x[q][j] - m_run[S::RSPLIT ? q : 0]);
+            psum[S::RSPLIT ? q : 0] += pj;
+            pb[4 * q + j] = (__bf16)pj;
           }
-        l_run += psum;
+#pragma unroll
+        for (int e = 0; e < S::NE; ++e) l_run[e] += psum[e];
         return pb;
       };
       // scores of tile itq (K operands through a ring of KRING reads) with the
       // gathers of tile itd interleaved, one 128-B line per four MFMAs
       auto scores = [&](int itq, f32x4* out) {
         const LDS_AS uint8_t* tp = tptr(itq);
+        if constexpr (S::RSPLIT) {
+          // k-step kk's K operand (this wave's 16 rows) feeds the MFMAs of both
+          // head groups; chain (group, kk mod 2) is fed every 4th MFMA
+          constexpr int KR = 4;
+          bf16x8 kr[18];
+#pragma unroll
+          for (int i = 0; i < KR; ++i)
+            kr[i] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + krs[i & 1] + (i >> 1) * S::RT * 128);
+          __builtin_amdgcn_sched_group_barrier(0x100, KR, 0);
+          f32x4 acc[2][2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) acc[e][0] = acc[e][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < 18; ++kk) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+              acc[e][kk & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[kk], qb[18 * e + kk], acc[e][kk & 1], 0, 0, 0);
+            const int j = kk + KR;
+            if (j < 18) kr[j] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + krs[j & 1] + (j >> 1) * S::RT * 128);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            if (j < 18) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+#pragma unroll
+          for (int e = 0; e < 2; ++e) out[e] = acc[e][0] + acc[e][1];
+          return;
+        }
         // MFMA i is (fragment i & 1, k-step i >> 1); it accumulates into chain
         // (fragment, k-step mod 4), so each of the 8 chains is fed every 8th MFMA
         // and no MFMA waits for its predecessor's result
@@ -906,37 +988,50 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         }
         wait_vm<(S::NST - 1) * S::PER>();
         lds_barrier();
+        // P of tile i is published into exchange buffer i & 1 at the end of
+        // step i - 1 (the prologue for tile 0); the barrier that opens step i
+        // makes it visible, and the buffer's previous readers (step i - 2's
+        // P.V operands) finished before that barrier
+        LDS_AS bf16x8* pex = (LDS_AS bf16x8*)(lds + S::PEX_OFF);
+        auto publish = [&](const bf16x8& pbv, int buf) {
+          if constexpr (S::RSPLIT) {
+            // rows 16*(wave & 1) + 4*g4 + j of head groups 2*(wave >> 1) + e:
+            // the half of each group's B operand that this wave owns
+            LDS_AS uint8_t* pw = (LDS_AS uint8_t*)lds + S::PEX_OFF + buf * 4096 +
+                                 (2 * (wave >> 1) * 64 + lane) * 16 + (wave & 1) * 8;
+            *(LDS_AS bf16x4*)pw = __builtin_shufflevector(pbv, pbv, 0, 1, 2, 3);
+            *(LDS_AS bf16x4*)(pw + 64 * 16) = __builtin_shufflevector(pbv, pbv, 4, 5, 6, 7);
+          } else {
+            pex[buf * 256 + hg * 64 + lane] = pbv;
+          }
+        };
         f32x4 sc[2];
         scores(0, sc);
-        bf16x8 pb = softmax(0, sc);   // P of tile 0
+        publish(softmax(0, sc, true), 0);   // P of tile 0
         bf16x8 vpre[8];
 #pragma unroll
         for (int f = 0; f < 8; ++f) vpre[f] = read_vt(0, f);
-        LDS_AS bf16x8* pex = (LDS_AS bf16x8*)(lds + S::PEX_OFF);
         for (int it = 0; it < nit; ++it) {
           wait_vm<(S::NST - 2) * S::PER>();   // tile it+1 has landed (this wave's share)
           // every wave's reads of tile it (its V^T operands) have completed
-          // before any gather refills that slot
+          // before any gather refills that slot, and P of tile it is published
           asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          bf16x8 pall[4];
+#pragma unroll
+          for (int hf = 0; hf < 4; ++hf) pall[hf] = pex[(it & 1) * 256 + hf * 64 + lane];
           f32x4 scn[2];
           if (it + 1 < nit) {
             scores(it + 1, scn);
           } else {
             scn[0] = scn[1] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
-          // publish this head group's P of tile it, take all four
-          pex[hg * 64 + lane] = pb;
-          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-          bf16x8 pall[4];
-#pragma unroll
-          for (int hf = 0; hf < 4; ++hf) pall[hf] = pex[hf * 64 + lane];
           // P.V of tile it over this wave's 8 output fragments x 4 head groups;
           // each fragment's V^T registers are refilled from tile it+1 once used;
           // the gathers of tile it + NST (into tile it's slot, free since the
           // last step) and the softmax of tile it+1 run under these MFMAs
           // (past the list the softmax sees only masked rows: no effect)
           dma_prep(it + S::NST);
-          pb = softmax(it + 1, scn);
+          const bf16x8 pb = softmax(it + 1, scn, false);
 #pragma unroll
           for (int f = 0; f < 8; ++f) {
 #pragma unroll
@@ -946,6 +1041,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
             dma_line(f);
           }
           dma_line(8);
+          publish(pb, (it + 1) & 1);
         }
       }
     } else {
@@ -983,29 +1079,59 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
   }
   // rare: some tile exceeded the reference headroom -> recompute the row
   // (every wave of the work-group takes the same decision)
-  if (!__syncthreads_or(overflow ? 1 : 0)) break;
+  // (a work-group OR through one LDS word of the compaction counts, free
+  // here; __syncthreads_or would take LDS of its own beyond the tile ring)
+  {
+    volatile int* flag = reinterpret_cast<volatile int*>(smem + S::CNT_OFF);
+    if (tid == 0) *flag = 0;
+    __syncthreads();
+    if (overflow) *flag = 1;
+    __syncthreads();
+    const bool any = *flag != 0;
+    __syncthreads();
+    if (!any) break;
+  }
   if constexpr (S::PAIR) {
     LDS_AS float* mex = (LDS_AS float*)(lds + S::MEX_OFF);
-    mex[wave * 64 + lane] = m_seen;
+    mex[wave * 64 + lane] = m_seen[0];
     __syncthreads();
-    m_run = fmaxf(m_seen, mex[(wave ^ 1) * 64 + lane]);
+    m_run[0] = fmaxf(m_seen[0], mex[(wave ^ 1) * 64 + lane]);
+    __syncthreads();
+  } else if constexpr (S::RSPLIT) {
+    // the two waves holding a head's row halves take their common maximum
+    LDS_AS float* mex = (LDS_AS float*)(lds + S::PEX_OFF);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) mex[(wave * 2 + e) * 64 + lane] = m_seen[e];
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 2; ++e) m_run[e] = fmaxf(m_seen[e], mex[((wave ^ 1) * 2 + e) * 64 + lane]);
     __syncthreads();
   } else {
-    m_run = m_seen;
+    m_run[0] = m_seen[0];
   }
-  l_run = 0.f;
+#pragma unroll
+  for (int e = 0; e < S::NE; ++e) l_run[e] = 0.f;
   overflow = false;
 #pragma unroll
   for (int f = 0; f < 32; ++f) o[f] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   // ---- epilogue: merge the row groups of each head group, normalise, write
-  float l_tot = l_run + wave_xor(l_run, 16);
-  l_tot += wave_xor(l_tot, 32);
+  // statistics slot of (head group, row half): RSPLIT 2 * group + (wave & 1), else the wave
+  float l_tot[S::NE];
+#pragma unroll
+  for (int e = 0; e < S::NE; ++e) {
+    l_tot[e] = l_run[e] + wave_xor(l_run[e], 16);
+    l_tot[e] += wave_xor(l_tot[e], 32);
+  }
   __syncthreads();
   if (lane < 16) {
-    stat[(wave * 16 + lane) * 2 + 0] = m_run;
-    stat[(wave * 16 + lane) * 2 + 1] = l_tot;
+#pragma unroll
+    for (int e = 0; e < S::NE; ++e) {
+      const int slot = S::RSPLIT ? 2 * (2 * (wave >> 1) + e) + (wave & 1) : wave;
+      stat[(slot * 16 + lane) * 2 + 0] = m_run[e];
+      stat[(slot * 16 + lane) * 2 + 1] = l_tot[e];
+    }
   }
   if constexpr (S::DSPLIT) {
     // stage as if head group hf held all 32 output fragments (layout read below)
@@ -1031,15 +1157,19 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
     const int hgi = head >> 4, nn = head & 15;
     float M = NEG_INF;
 #pragma unroll
-    for (int r = 0; r < S::NRG; ++r) M = fmaxf(M, stat[((r * S::HG + hgi) * 16 + nn) * 2]);
+    for (int r = 0; r < S::NRG; ++r)
+      M = fmaxf(M, stat[(((S::RSPLIT ? 2 : 1) * (r * S::HG + hgi)) * 16 + nn) * 2]);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float L = 0.f;
     if (M != NEG_INF) {
 #pragma unroll
       for (int r = 0; r < S::NRG; ++r) {
         const int w = r * S::HG + hgi;
-        const float fct = fast_exp2(stat[(w * 16 + nn) * 2] - M);
-        L += fct * (stat[(w * 16 + nn) * 2 + 1] + (S::PAIR ? stat[((w + 1) * 16 + nn) * 2 + 1] : 0.f));
+        // PAIR: waves w, w+1 hold one head's row halves; RSPLIT: slots 2w, 2w+1
+        const int sw = S::RSPLIT ? 2 * w : w;
+        const float fct = fast_exp2(stat[(sw * 16 + nn) * 2] - M);
+        L += fct * (stat[(sw * 16 + nn) * 2 + 1] +
+                    ((S::PAIR || S::RSPLIT) ? stat[((sw + 1) * 16 + nn) * 2 + 1] : 0.f));
         // dims 8c..8c+7 = fragment c/2, lanes (2*(c&1) + {0,1})*16 + nn, j = 0..3
         const f32x4* ost = reinterpret_cast<const f32x4*>(smem) + (size_t)w * 32 * 64 + (c >> 1) * 64;
         const f32x4 v0 = ost[(2 * (c & 1) + 0) * 16 + nn];
@@ -1154,6 +1284,7 @@ using V_H2_A = Shape<2, 2, 32, 2, 0>;
 using V_H2_B = Shape<2, 1, 32, 4, 0>;
 using V_H4_A = Shape<4, 1, 32, 4, 0, true, true>;
 using V_H4_B = Shape<4, 1, 32, 4, 0>;
+using V_H4_C = Shape<4, 1, 32, 4, 0, true, true, false, true>;
 using F_H1_A = Shape<2, 2, 32, 3, 1, false, false, true>;
 using F_H1_B = Shape<1, 2, 32, 3, 1>;
 using F_H2_A = Shape<2, 1, 32, 4, 1>;
@@ -1186,8 +1317,8 @@ bool fwd_shape(int kv_format, int head_groups, int variant, FwdShape* shape) {
     case 1: *shape = variant == 1 ? shape_of<V_H1_B>() : shape_of<V_H1_A>(); return variant <= 1;
     case 2: *shape = variant == 1 ? shape_of<V_H2_B>() : shape_of<V_H2_A>(); return variant <= 1;
     case 4:
-      *shape = variant == 1 ? shape_of<V_H4_B>() : shape_of<V_H4_A>();
-      return variant <= 1;
+      *shape = variant == 2 ? shape_of<V_H4_C>() : variant == 1 ? shape_of<V_H4_B>() : shape_of<V_H4_A>();
+      return variant <= 2;
     default: return false;
   }
 }
@@ -1205,7 +1336,10 @@ hipError_t launch_fwd(const FwdArgs& a, int kv_format, int head_groups, int vari
   switch (head_groups) {
     case 1: return variant == 1 ? launch_one<V_H1_B>(a, grid, stream) : launch_one<V_H1_A>(a, grid, stream);
     case 2: return variant == 1 ? launch_one<V_H2_B>(a, grid, stream) : launch_one<V_H2_A>(a, grid, stream);
-    case 4: return variant == 1 ? launch_one<V_H4_B>(a, grid, stream) : launch_one<V_H4_A>(a, grid, stream);
+    case 4:
+      return variant == 2   ? launch_one<V_H4_C>(a, grid, stream)
+             : variant == 1 ? launch_one<V_H4_B>(a, grid, stream)
+                            : launch_one<V_H4_A>(a, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

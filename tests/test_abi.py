@@ -70,7 +70,7 @@ def test_zero_tokens_is_noop():
     (dict(kernel_variant=1, kv_format="fp8", num_heads=32), B.SMLA_ERR_UNSUPPORTED),
     (dict(kernel_variant=2, kv_format="fp8"), B.SMLA_ERR_UNSUPPORTED),
     (dict(kernel_variant=2), B.SMLA_ERR_UNSUPPORTED),                 # h = 8: no third shape
-    (dict(kernel_variant=2, num_heads=64), B.SMLA_ERR_UNSUPPORTED),
+    (dict(kernel_variant=3, num_heads=64), B.SMLA_ERR_UNSUPPORTED),
 ])
 def test_bad_params_rejected(kw, code):
     assert _fwd(_params(**kw)) == code

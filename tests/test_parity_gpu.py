@@ -45,7 +45,8 @@ def test_mini_heads(h):
 @pytest.mark.parametrize("h,tiling,variant", [(8, "pad64", 0), (16, "pad64", 0), (8, "native", 1),
                                                (16, "native", 1), (32, "native", 1), (24, "native", 1),
                                                (64, "native", 1), (40, "native", 1), (8, "pad64", 1),
-                                               (48, "native", 1), (16, "pad64", 1)])
+                                               (48, "native", 1), (16, "pad64", 1), (64, "native", 2),
+                                               (40, "native", 2), (33, "native", 2), (8, "pad64", 2)])
 def test_mini_tilings_and_variants(h, tiling, variant):
     say("mini tiling", h, tiling, variant)
     c = G.make_mini(seed=22, num_heads=h, topk=300)
@@ -123,13 +124,13 @@ def test_repeated_index_returns_row_exactly(k):
     check(out, lse, ro, rl, "repeated index")
 
 
-@pytest.mark.parametrize("splits", [1, 3])
-def test_large_score_spread_recomputes_exactly(splits):
+@pytest.mark.parametrize("splits,h,variant", [(1, 16, 0), (3, 16, 0), (1, 64, 2), (3, 64, 2)])
+def test_large_score_spread_recomputes_exactly(splits, h, variant):
     """A row whose later entries score far above its first tile (beyond the
     kernel's exponent headroom) forces the one-time recomputation with the
     exact maximum; the result must still match the oracle."""
-    say("large score spread", splits)
-    c = G.make_mini(seed=41, num_heads=16, topk=300, drop_frac=0.0)
+    say("large score spread", splits, h, variant)
+    c = G.make_mini(seed=41, num_heads=h, topk=300, drop_frac=0.0)
     kv = c.kv.copy()
     flat = kv.reshape(-1, 576)
     hot = 5                                           # physical row made to align with every query
@@ -141,7 +142,7 @@ def test_large_score_spread_recomputes_exactly(splits):
     sidx = slot_indices(c2)
     sidx[:, -1] = hot                                 # last entry of every row: the hot row
     dev = Dev(c2, idx=sidx)
-    out, lse = to_np(*run_gpu(dev, logical=False, num_splits=splits))
+    out, lse = to_np(*run_gpu(dev, logical=False, num_splits=splits, variant=variant))
     from oracle import sparse_mla_oracle as O
     ro, rl = O.sparse_mla_forward(c2.q, c2.kv, sidx, topk=c2.topk, scale=c2.scale, index_mode="slot")
     check(out, lse, ro, rl, "score spread")
@@ -196,6 +197,47 @@ def test_deterministic():
     a = to_np(*run_gpu(dev, num_splits=3))
     b = to_np(*run_gpu(dev, num_splits=3))
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("topk", [5, 16, 17, 40])
+def test_h64_row_split_short_lists(topk):
+    """h = 64 with the row-half score split: lists of at most 16 rows leave the
+    second row half of every tile empty, so its head references come from the
+    partner wave alone."""
+    say("h64 row split short lists", topk)
+    c = G.make_mini(seed=61, num_heads=64, topk=topk, drop_frac=0.2)
+    dev = Dev(c)
+    out, lse = to_np(*run_gpu(dev, variant=2, num_splits=1))
+    check(out, lse, *oracle(c), what="h64 v2 topk %d" % topk)
+
+
+def test_h64_row_split_empty_rows_and_long_lists():
+    say("h64 row split empty rows / topk 5000")
+    c = G.make_mini(seed=62, num_heads=64, topk=100)
+    idx = c.topk_idx.copy()
+    idx[0, :] = -1
+    idx[3, 1:] = -1                     # a single valid entry
+    dev = Dev(c, idx=idx)
+    out, lse = to_np(*run_gpu(dev, variant=2))
+    check(out, lse, *oracle(c, idx=idx), what="h64 v2 empty rows")
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+    c = G.build_case("big_topk", seed=63, hist=[9000], new=[6], num_heads=64, topk=5000, drop_frac=0.05)
+    dev = Dev(c)
+    for splits in (1, 3):
+        out, lse = to_np(*run_gpu(dev, variant=2, num_splits=splits))
+        check(out, lse, *oracle(c), what="h64 v2 topk 5000 s%d" % splits)
+
+
+def test_h64_row_split_matches_default_shape():
+    """Both h = 64 shapes run the same arithmetic per element up to the order
+    of the k-step accumulation, so they agree within the split tolerance."""
+    say("h64 v2 vs v0")
+    c = G.make_mini(seed=64, num_heads=64, topk=300)
+    dev = Dev(c)
+    o0, l0 = to_np(*run_gpu(dev, variant=0))
+    o2, l2 = to_np(*run_gpu(dev, variant=2))
+    assert np.max(np.abs(o0 - o2)) <= SPLIT_ATOL * 8
+    assert np.max(np.abs(l0 - l2)) <= SPLIT_ATOL
 
 
 def test_strided_outputs_and_guard_bands():
