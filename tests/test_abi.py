@@ -134,6 +134,10 @@ def test_plan_for_is_pure_and_splits_small_batches():
     # large batch: unsplit
     pl = B.plan(_params(num_tokens=4096, topk=2048), num_cus=256)
     assert pl.num_splits == 1 and pl.workspace_bytes == 0 and pl.grid == 4096
+    pl = B.plan(_params(num_tokens=50, topk=2048, num_heads=64), num_cus=256)
+    assert pl.num_splits == 5 and pl.units == 250 and pl.grid == 256
+    pl = B.plan(_params(num_tokens=20, topk=256, num_heads=64), num_cus=256)
+    assert pl.num_splits == 8 and pl.units == 160 and pl.grid == 160
     # head tiles
     assert B.plan(_params(num_heads=32), num_cus=256).head_groups == 2
     assert B.plan(_params(num_heads=64), num_cus=256).head_groups == 4

@@ -240,6 +240,43 @@ def test_h64_row_split_matches_default_shape():
     assert np.max(np.abs(l0 - l2)) <= SPLIT_ATOL
 
 
+@pytest.mark.parametrize("variant,splits", [(0, 1), (2, 1), (0, 3)])
+def test_h64_many_units(variant, splits):
+    """h = 64 with more work units than CUs (a second wave of work-groups on
+    every CU), unsplit and split."""
+    say("h64 many units", variant, splits)
+    c = G.make_mini(seed=65, num_heads=64, topk=300, num_seqs=24, tokens_per_seq=30)
+    assert c.num_tokens * splits > 2 * 256
+    dev = Dev(c)
+    out, lse = to_np(*run_gpu(dev, variant=variant, num_splits=splits))
+    check(out, lse, *oracle(c), what="h64 many units v%d s%d" % (variant, splits))
+
+
+def test_h64_many_rows_recompute_and_two_chunks():
+    """Many h = 64 rows where every third one needs the recomputation pass,
+    and rows of two compaction passes."""
+    say("h64 many rows: recompute / two chunks")
+    c = G.make_mini(seed=66, num_heads=64, topk=300, num_seqs=24, tokens_per_seq=30, drop_frac=0.0)
+    kv = c.kv.copy()
+    flat = kv.reshape(-1, 576)
+    hot = 5
+    qsign = np.sign((c.q[0, 0].astype(np.uint32) << 16).view(np.float32))
+    flat[hot] = G.to_bf16_bits((16.0 * qsign).astype(np.float32))
+    c2 = G.Case(**{**c.__dict__, "kv": kv})
+    sidx = slot_indices(c2)
+    sidx[::3, -1] = hot                              # every third row gets the hot row last
+    dev = Dev(c2, idx=sidx)
+    from oracle import sparse_mla_oracle as O
+    ro, rl = O.sparse_mla_forward(c2.q, c2.kv, sidx, topk=c2.topk, scale=c2.scale, index_mode="slot")
+    for variant in (0, 2):
+        out, lse = to_np(*run_gpu(dev, logical=False, num_splits=1, variant=variant))
+        check(out, lse, ro, rl, "h64 many rows spread v%d" % variant)
+    c = G.build_case("two_chunks", seed=67, hist=[6000, 7000], new=[160, 160], num_heads=64, topk=2100,
+                     drop_frac=0.05)
+    out, lse = to_np(*run_gpu(Dev(c), num_splits=1))
+    check(out, lse, *oracle(c), what="h64 topk 2100")
+
+
 def test_strided_outputs_and_guard_bands():
     say("guard bands")
     c = G.make_mini(seed=33, num_heads=8, topk=200)
