@@ -21,7 +21,11 @@ query row t:
      PR #55738, "Key source snippets": nope part first, rope part last; vLLM
      PR #60220, "Claims": q rows are 576 wide).  bf16 rows are upcast
      exactly; fp8 rows are code value x block scale for the latent part (one
-     fp32 scale per 128 dims) and bf16 for the rope part.
+     fp32 scale per 128 dims) and bf16 for the rope part.  In the NoPE
+     geometry the rope part has zero width and rows are the 512 latent dims
+     (prhub report on vLLM PR #55738, "Details" items 1 and 3: qk_rope 0, and
+     the K concat with an empty rope part is the latent part itself); the
+     width is taken from q (bf16 caches only).
   4. All h heads of the row share the gathered rows (MQA / absorbed form,
      prhub report on PR #55738, "Motivation": the per-token top-k MQA
      kernel).  Scores S = (Q @ R^T) * scale.
@@ -115,15 +119,19 @@ def fp8_rows(kv_pages: np.ndarray, slots: np.ndarray, page_size: int):
     return codes, scales, rope_bits
 
 
-def gather_rows(kv: np.ndarray, slots, kv_format: str, page_size: int, dtype=np.float64) -> np.ndarray:
-    """Step 3: the listed cache rows as an explicit [n, 576] array."""
+def gather_rows(kv: np.ndarray, slots, kv_format: str, page_size: int, dtype=np.float64,
+                d_qk: int = D_QK) -> np.ndarray:
+    """Step 3: the listed cache rows as an explicit [n, d_qk] array (576, or
+    512 in the NoPE geometry)."""
     slots = np.asarray(slots, dtype=np.int64)
     n = slots.shape[0]
-    R = np.zeros((n, D_QK), dtype=dtype)
+    if d_qk not in (D_QK, D_LATENT) or (d_qk != D_QK and kv_format != "bf16"):
+        raise ValueError("row width %d with %s cache" % (d_qk, kv_format))
+    R = np.zeros((n, d_qk), dtype=dtype)
     if n == 0:
         return R
     if kv_format == "bf16":
-        flat = kv.reshape(-1, D_QK)
+        flat = kv.reshape(-1, d_qk)
         R[:] = bf16_to_float(flat[slots], dtype)
     elif kv_format == "fp8":
         codes, scales, rope = fp8_rows(kv, slots, page_size)
@@ -150,7 +158,8 @@ def row_slots(topk_idx_row: np.ndarray, topk: int, index_mode: str, page_size: i
 # ---------------------------------------------------------------- attention
 
 def attend(Q: np.ndarray, R: np.ndarray, scale: float):
-    """Steps 4-6 for one query row: Q [h, 576], R [n, 576] -> (out [h, 512], lse [h])."""
+    """Steps 4-6 for one query row: Q [h, d], R [n, d] -> (out [h, 512], lse [h]),
+    d = 576 (or 512 in the NoPE geometry)."""
     h = Q.shape[0]
     if R.shape[0] == 0:
         return np.zeros((h, D_LATENT), dtype=Q.dtype), np.full(h, -np.inf, dtype=Q.dtype)
@@ -167,8 +176,9 @@ def sparse_mla_forward(q: np.ndarray, kv: np.ndarray, topk_idx: np.ndarray, *, t
                        scale: float, kv_format: str = "bf16", page_size: int = 64,
                        index_mode: str = "logical", block_table=None, token_seq=None,
                        num_heads=None, rows=None, dtype=np.float64):
-    """The whole definition.  q: uint16 bf16 bits [T, H, 576]; kv: the paged
-    cache (bf16 bits [pages, P, 576] or fp8 bytes [pages, page_bytes]);
+    """The whole definition.  q: uint16 bf16 bits [T, H, 576] ([T, H, 512]
+    for the NoPE geometry); kv: the paged cache (bf16 bits [pages, P, d] with
+    the same d, or fp8 bytes [pages, page_bytes]);
     topk_idx: int32 [T, >= topk].  Returns (out [n, h, 512], lse [n, h]) for
     the requested rows (all rows by default)."""
     T = q.shape[0]
@@ -181,7 +191,7 @@ def sparse_mla_forward(q: np.ndarray, kv: np.ndarray, topk_idx: np.ndarray, *, t
     for i, t in enumerate(rows):
         seq = int(token_seq[t]) if token_seq is not None else 0
         slots = row_slots(topk_idx[t], topk, index_mode, page_size, num_slots, block_table, seq)
-        R = gather_rows(kv, slots, kv_format, page_size, dtype)
+        R = gather_rows(kv, slots, kv_format, page_size, dtype, d_qk=q.shape[2])
         Q = bf16_to_float(q[t, :h], dtype)
         out[i], lse[i] = attend(Q, R, scale)
     return out, lse

@@ -10,7 +10,9 @@ Workload shapes follow the pages' workloads:
   * rows are 576 wide = 512 latent dims + 64 rope dims, latent first
     (vLLM PR #60220, "Claims": q is T x 64 x 576, out is T x 64 x 512;
     prhub report on vLLM PR #55738, "Key source snippets": nope part first,
-    rope part last);
+    rope part last); with `rope_dims=0` the NoPE geometry: rows are the
+    512 latent dims alone (prhub report on vLLM PR #55738, "Details" items 1
+    and 3: a zero-width rope part);
   * top-k = 2048 int32 indices per query row (vLLM PR #54951, "Summary");
   * the cache is paged, 64 tokens per page, and -1 marks a skipped entry
     (the plainest reading of the paged, slot-mapped cache that PR #54951's
@@ -44,8 +46,8 @@ def fp8_page_bytes(page_size: int) -> int:
 class Case:
     """One synthetic batch.  All arrays are host numpy arrays.
 
-    q            uint16 [T, H, 576]   bf16 bit patterns
-    kv           bf16: uint16 [num_pages, page_size, 576]
+    q            uint16 [T, H, 576]   bf16 bit patterns ([T, H, 512] for NoPE)
+    kv           bf16: uint16 [num_pages, page_size, 576] ([.., 512] for NoPE)
                  fp8 : uint8  [num_pages, fp8_page_bytes(page_size)]
     block_table  int32  [num_seqs, max_blocks]  physical page of each logical block
     token_seq    int32  [T]  sequence of each query row
@@ -76,6 +78,11 @@ class Case:
     @property
     def num_tokens(self) -> int:
         return int(self.q.shape[0])
+
+    @property
+    def rope_dims(self) -> int:
+        """64 (rows of 512 latent + 64 rope dims) or 0 (NoPE: latent only)."""
+        return int(self.q.shape[2]) - D_LATENT
 
     @property
     def num_pages(self) -> int:
@@ -213,10 +220,14 @@ def sample_topk(rng, p: np.ndarray, k: int, local_frac: float = 0.0, local_win: 
 def build_case(name: str, *, seed: int, hist: list, new: list, num_heads: int, topk: int,
                page_size: int = 64, kv_format: str = "bf16", idx_stride: Optional[int] = None,
                drop_frac: float = 0.0, local_frac: float = 0.0, extra_pages: int = 0,
-               scale: float = SCALE_1_OVER_24, query_positions: Optional[list] = None) -> Case:
+               scale: float = SCALE_1_OVER_24, query_positions: Optional[list] = None,
+               rope_dims: int = D_ROPE) -> Case:
     """Generic builder: sequence s holds hist[s] + new[s] cached tokens and
     contributes new[s] query rows at positions hist[s] .. hist[s] + new[s] - 1
-    (unless `query_positions[s]` lists them explicitly)."""
+    (unless `query_positions[s]` lists them explicitly).  rope_dims 0 draws
+    the NoPE geometry (512-wide q and bf16 cache rows)."""
+    assert rope_dims in (0, D_ROPE) and (rope_dims == D_ROPE or kv_format == "bf16")
+    d_qk = D_LATENT + rope_dims
     rng = np.random.default_rng(seed)
     seq_lens = np.array([h + n for h, n in zip(hist, new)], dtype=np.int64)
     # 1. block tables
@@ -244,11 +255,11 @@ def build_case(name: str, *, seed: int, hist: list, new: list, num_heads: int, t
         full[:, topk:] = rng.integers(0, 4, size=(T, stride - topk), dtype=np.int32)
         idx = full
     # 4. q
-    q = normal_bf16(rng, (T, num_heads, D_QK))
+    q = normal_bf16(rng, (T, num_heads, d_qk))
     # 5. kv
     codes = scales = rope = None
     if kv_format == "bf16":
-        kv = normal_bf16(rng, (num_pages, page_size, D_QK))
+        kv = normal_bf16(rng, (num_pages, page_size, d_qk))
     elif kv_format == "fp8":
         nslots = num_pages * page_size
         scales = np.exp2(rng.uniform(-4.0, 4.0, size=(nslots, D_LATENT // 128))).astype(np.float32)
@@ -323,7 +334,7 @@ def make_config(name: str, seed: Optional[int] = None, **kw) -> Case:
 
 def make_mini(seed: int = 7, num_heads: int = 8, topk: int = 300, kv_format: str = "bf16",
               num_seqs: int = 3, tokens_per_seq: int = 12, hist: int = 900, drop_frac: float = 0.1,
-              idx_stride: Optional[int] = None, page_size: int = 64) -> Case:
+              idx_stride: Optional[int] = None, page_size: int = 64, rope_dims: int = D_ROPE) -> Case:
     """A small batch the oracle finishes in well under a second: several tiles
     per row, a ragged tail (topk not a multiple of 16), short prefixes padded
     with -1 (the first rows of each sequence may sit at small positions), and
@@ -335,7 +346,7 @@ def make_mini(seed: int = 7, num_heads: int = 8, topk: int = 300, kv_format: str
         qpos.append(ps)
     return build_case("mini", seed=seed, hist=[hist] * num_seqs, new=[tokens_per_seq] * num_seqs,
                       num_heads=num_heads, topk=topk, kv_format=kv_format, idx_stride=idx_stride,
-                      drop_frac=drop_frac, page_size=page_size, query_positions=qpos)
+                      drop_frac=drop_frac, page_size=page_size, query_positions=qpos, rope_dims=rope_dims)
 
 
 class DeviceCase:

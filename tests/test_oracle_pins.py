@@ -22,12 +22,12 @@ SCALE = G.SCALE_1_OVER_24
 
 
 def _paged_from_contiguous(rng, K_bits, page_size):
-    """Scatter a contiguous [N, 576] bf16 sequence into randomly permuted pages
+    """Scatter a contiguous [N, d] bf16 sequence into randomly permuted pages
     (test-side paging, independent of the oracle's translation)."""
     N = K_bits.shape[0]
     npages = (N + page_size - 1) // page_size
     perm = rng.permutation(npages)
-    kv = np.zeros((npages, page_size, O.D_QK), dtype=np.uint16)
+    kv = np.zeros((npages, page_size, K_bits.shape[1]), dtype=np.uint16)
     for blk in range(npages):
         rows = K_bits[blk * page_size:(blk + 1) * page_size]
         kv[perm[blk], :rows.shape[0]] = rows
@@ -35,10 +35,10 @@ def _paged_from_contiguous(rng, K_bits, page_size):
     return kv, bt
 
 
-def _dense_case(h, N=256, T=32, seed=3, page_size=64):
+def _dense_case(h, N=256, T=32, seed=3, page_size=64, d=O.D_QK):
     rng = np.random.default_rng(seed)
-    K_bits = G.normal_bf16(rng, (N, O.D_QK))
-    q_bits = G.normal_bf16(rng, (T, h, O.D_QK))
+    K_bits = G.normal_bf16(rng, (N, d))
+    q_bits = G.normal_bf16(rng, (T, h, d))
     pos = np.sort(rng.choice(N, size=T, replace=False)).astype(np.int32)
     pos[0] = 0                         # a row that sees a single key
     pos[-1] = N - 1                    # a row that sees everything
@@ -49,20 +49,21 @@ def _dense_case(h, N=256, T=32, seed=3, page_size=64):
     return K_bits, q_bits, pos, kv, bt, idx
 
 
-@pytest.mark.parametrize("h", [1, 8])
-def test_dense_causal_equals_sdpa(h):
+@pytest.mark.parametrize("h,d", [(1, O.D_QK), (8, O.D_QK), (8, O.D_LATENT)])
+def test_dense_causal_equals_sdpa(h, d):
     """When every row lists its whole causal prefix, sparse attention is dense
     causal MQA: compare with torch's scaled_dot_product_attention in fp64 (K
     shared by all heads, V = the first 512 dims, boolean causal mask) and
-    torch.logsumexp for lse."""
-    K_bits, q_bits, pos, kv, bt, idx = _dense_case(h)
+    torch.logsumexp for lse.  d = 512 is the NoPE geometry (no rope part: K
+    and V are the same 512 dims)."""
+    K_bits, q_bits, pos, kv, bt, idx = _dense_case(h, d=d)
     T, N = idx.shape
     out, lse = O.sparse_mla_forward(q_bits, kv, idx, topk=N, scale=SCALE, page_size=64,
                                     index_mode="logical", block_table=bt,
                                     token_seq=np.zeros(T, np.int32))
     Kf = torch.from_numpy(O.bf16_to_float(K_bits))                     # [N, 576]
     Qf = torch.from_numpy(O.bf16_to_float(q_bits)).permute(1, 0, 2)     # [h, T, 576]
-    k = Kf[None].expand(h, N, O.D_QK).contiguous()
+    k = Kf[None].expand(h, N, d).contiguous()
     v = Kf[None, :, :O.D_LATENT].expand(h, N, O.D_LATENT).contiguous()
     mask = torch.arange(N)[None, :] <= torch.from_numpy(pos.astype(np.int64))[:, None]   # [T, N]
     ref = torch.nn.functional.scaled_dot_product_attention(Qf[None], k[None], v[None],
@@ -73,6 +74,22 @@ def test_dense_causal_equals_sdpa(h):
     ref_lse = torch.logsumexp(S, dim=-1).permute(1, 0).numpy()          # [T, h]
     np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+
+
+def test_nope_equals_zero_rope_parts():
+    """The NoPE geometry is the 576-wide definition with the rope dims of q and
+    of every cache row set to zero (those dims then add nothing to any score)."""
+    c = G.make_mini(seed=15, num_heads=5, topk=150, num_seqs=2, tokens_per_seq=7, rope_dims=0)
+    assert c.q.shape[2] == 512 and c.kv.shape[2] == 512
+    kw = dict(topk=c.topk, scale=c.scale, index_mode="logical", block_table=c.block_table,
+              token_seq=c.token_seq)
+    out, lse = O.sparse_mla_forward(c.q, c.kv, c.topk_idx, **kw)
+    pad = lambda x: np.concatenate([x, np.zeros(x.shape[:-1] + (O.D_ROPE,), np.uint16)], axis=-1)
+    out_p, lse_p = O.sparse_mla_forward(pad(c.q), pad(c.kv), c.topk_idx, **kw)
+    np.testing.assert_allclose(out, out_p, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse, lse_p, rtol=1e-13, atol=1e-14)
+    with pytest.raises(ValueError):
+        O.gather_rows(c.kv, [0], "fp8", 64, d_qk=O.D_LATENT)
 
 
 def test_index_order_invariance():
