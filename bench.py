@@ -17,7 +17,8 @@ host.
 Workloads (synthetic, seeded; `--workload`):
   c2_decode (default)  32 rows x 1 query, h=8, 16384-token contexts
   c1_tiny              64 rows, h=8, topk=128
-  c3_h{8,16,32,64}     4096 rows over 8 x (8192 + 512) tokens; suffix _pad64 for the padded tiling
+  c3_h{8,16,32,64}     4096 rows over 8 x (8192 + 512) tokens; suffix _pad64 for the padded tiling,
+                       _nope for the NoPE geometry (512-wide rows, no rope part)
   c4_long_prefill      16384 rows, h=64, 65536-token history, locality-biased indices
 """
 from __future__ import annotations
@@ -59,14 +60,18 @@ def parse():
 def workload(name):
     from sparse_mla_attention_04_amd import inputs as G
     tiling = "native"
+    rope = 64
+    if name.endswith("_nope"):
+        rope = 0
+        name = name[:-len("_nope")]
     if name.endswith("_pad64"):
         tiling = "pad64"
         name = name[:-len("_pad64")]
     if name.startswith("c3_h"):
         h = int(name[len("c3_h"):])
-        case = G.make_config("c3_sweep").with_heads(h)
-        return case, tiling, "c3_sweep"
-    if name in ("c1_tiny", "c2_decode", "c4_long_prefill", "c5_fp8"):
+        case = G.make_config("c3_sweep", rope_dims=rope).with_heads(h)
+        return case, tiling, "c3_sweep" if rope else "c3_sweep_nope"
+    if name in ("c1_tiny", "c2_decode", "c4_long_prefill", "c5_fp8") and rope:
         return G.make_config(name), tiling, name
     raise SystemExit("unknown workload %s" % name)
 
@@ -256,9 +261,10 @@ def main():
     del flush
 
     n_valid = algorithmic_counts(case)
-    row_bytes = 1152 if case.kv_format == "bf16" else 656
+    d_qk = int(case.q.shape[2])
+    row_bytes = 2 * d_qk if case.kv_format == "bf16" else 656
     gathered = n_valid * row_bytes
-    flops = n_valid * h * 2 * (576 + 512)
+    flops = n_valid * h * 2 * (d_qk + 512)
     tokens_per_s = T / (ms_per_step * 1e-3)
     hbm_bound = h < 64
     if hbm_bound:

@@ -24,10 +24,15 @@
  *     row, stored in buffers wider than top-k (2051 columns).
  *   - vLLM PR #64510, section "Details": the real head count (8/16/32) is
  *     run natively instead of padding heads to 64.
+ *   - prhub report on vLLM PR #55738, "Details" items 1 and 3: a NoPE MLA
+ *     layout has a zero-width rope part (qk_rope 0), and K is then the
+ *     latent part alone (SMLA_GEOM_NOPE below).
  *
  * Conventions fixed by this ABI (the pages leave them open):
  *   - A cache row is 576 values: dims 0..511 latent, 512..575 rope.  The
- *     value vector of a row is its first 512 dims.
+ *     value vector of a row is its first 512 dims.  With geometry
+ *     SMLA_GEOM_NOPE rows and query heads are the 512 latent dims alone
+ *     (bf16 cache only: row `slot` at byte slot * 1024).
  *   - The cache is paged; page_size rows per page (a power of two; 64 in
  *     the configurations this library is tuned for).
  *       bf16 cache: row `slot` lives at byte slot * 1152.
@@ -91,6 +96,14 @@ extern "C" {
 #define SMLA_TILING_NATIVE 1
 #define SMLA_TILING_PAD64 2
 
+/* geometry (smla_params.geometry): the width of query heads and cache rows.
+ * MLA: 576 = 512 latent + 64 rope dims.  NOPE: 512 latent dims, no rope
+ * part (bf16 caches, kernel_variant 0; anything else -> SMLA_ERR_UNSUPPORTED).
+ * The output is 512 wide either way.  0 is MLA, so zero-initialised params
+ * keep the rope part. */
+#define SMLA_GEOM_MLA 0
+#define SMLA_GEOM_NOPE 1
+
 /* Gather order (smla_params.gather_order).  LIST follows the index list;
  * SLOT groups each row's entries (stably) into 16 ranges of physical cache
  * row, so that the rows computed at the same time on one XCD read nearby
@@ -114,7 +127,8 @@ typedef struct smla_params {
   int32_t page_size;           /* rows per cache page, power of two in [1, 4096]      */
   int64_t idx_stride;          /* int32 elements between index rows, >= topk          */
   int64_t q_stride_t;          /* bf16 elements between query rows (multiple of 8)    */
-  int64_t q_stride_h;          /* bf16 elements between heads (>= 576, multiple of 8) */
+  int64_t q_stride_h;          /* bf16 elements between heads (>= 576, or >= 512 for  */
+                               /* SMLA_GEOM_NOPE; multiple of 8)                      */
   int64_t out_stride_t;        /* bf16 elements between output rows (multiple of 8)   */
   int64_t out_stride_h;        /* bf16 elements between output heads (>= 512, mult 8) */
   int64_t lse_stride_t;        /* fp32 elements between lse rows (>= h)               */
@@ -134,6 +148,7 @@ typedef struct smla_params {
   int32_t gather_order;        /* SMLA_GATHER_*: order in which a row's listed cache  */
                                /* rows are gathered (the result is the same set sum;  */
                                /* fp32 summation order, hence rounding, follows it)   */
+  int32_t geometry;            /* SMLA_GEOM_*: row width (576 with rope, 512 NoPE)    */
 } smla_params;
 
 /* Read-only description of how a call with these parameters is executed. */
@@ -173,8 +188,10 @@ int sparse_mla_plan(const smla_params* p, smla_plan* plan);
 int sparse_mla_plan_for(const smla_params* p, int32_t num_cus, smla_plan* plan);
 
 /* The forward pass.  Device pointers:
- *   q           bf16  [T, h, 576] with strides q_stride_t / q_stride_h (16-B aligned)
- *   kv_cache    bf16 [num_pages, page_size, 576] or the fp8 page layout above (16-B aligned)
+ *   q           bf16  [T, h, 576] ([T, h, 512] for SMLA_GEOM_NOPE) with strides
+ *               q_stride_t / q_stride_h (16-B aligned)
+ *   kv_cache    bf16 [num_pages, page_size, 576] ([.., 512] for SMLA_GEOM_NOPE) or the
+ *               fp8 page layout above (16-B aligned)
  *   block_table int32 [num_seqs, block_table_stride]  (LOGICAL mode; NULL in SLOT mode)
  *   token_seq   int32 [T]                             (LOGICAL mode; NULL in SLOT mode)
  *   topk_idx    int32 [T, idx_stride]                 (4-B aligned)

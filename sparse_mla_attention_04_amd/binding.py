@@ -26,6 +26,7 @@ KV_FORMATS = {"bf16": 0, "fp8": 1}
 INDEX_MODES = {"slot": 0, "logical": 1}
 TILINGS = {"auto": 0, "native": 1, "pad64": 2}
 GATHER_ORDERS = {"auto": 0, "list": 1, "slot": 2}
+GEOMETRIES = {"mla": 0, "nope": 1}
 D_QK, D_V = 576, 512
 
 EXPORTS = ("sparse_mla_workspace_size", "sparse_mla_plan", "sparse_mla_plan_for",
@@ -46,7 +47,7 @@ class Params(ctypes.Structure):
         ("block_table_stride", ctypes.c_int64),
         ("softmax_scale", ctypes.c_float), ("tiling", ctypes.c_int32),
         ("num_splits", ctypes.c_int32), ("kernel_variant", ctypes.c_int32),
-        ("gather_order", ctypes.c_int32),
+        ("gather_order", ctypes.c_int32), ("geometry", ctypes.c_int32),
     ]
 
 
@@ -113,12 +114,13 @@ def make_params(*, num_tokens: int, num_heads: int, topk: int, idx_stride: Optio
                 index_mode: str = "logical", num_seqs: int = 0, max_blocks_per_seq: int = 0,
                 block_table_stride: Optional[int] = None, scale: float = 1.0 / 24.0,
                 tiling: str = "auto", num_splits: int = 0, kernel_variant: int = 0,
-                gather_order: str = "auto",
+                gather_order: str = "auto", geometry: str = "mla",
                 q_strides=None, out_strides=None, lse_stride: Optional[int] = None) -> Params:
     p = Params()
     p.num_tokens, p.num_heads, p.topk, p.page_size = num_tokens, num_heads, topk, page_size
     p.idx_stride = topk if idx_stride is None else idx_stride
-    qs = q_strides or (num_heads * D_QK, D_QK)
+    d_qk = D_V if geometry == "nope" else D_QK
+    qs = q_strides or (num_heads * d_qk, d_qk)
     os_ = out_strides or (num_heads * D_V, D_V)
     p.q_stride_t, p.q_stride_h = qs
     p.out_stride_t, p.out_stride_h = os_
@@ -133,6 +135,7 @@ def make_params(*, num_tokens: int, num_heads: int, topk: int, idx_stride: Optio
     p.num_splits = num_splits
     p.kernel_variant = kernel_variant
     p.gather_order = GATHER_ORDERS[gather_order]
+    p.geometry = GEOMETRIES[geometry]
     return p
 
 
@@ -162,7 +165,8 @@ def params_for(q, kv, topk_idx, out, lse, *, topk: int, scale: float, page_size:
                num_splits: int = 0, kernel_variant: int = 0, gather_order: str = "auto") -> Params:
     """smla_params from tensors: q bf16 [T, h, 576] (last dim contiguous), kv the
     cache pool (bf16 [pages, P, 576] or uint8 [pages, P * 656]), topk_idx int32
-    [T, >= topk], out bf16 [T, h, 512], lse fp32 [T, h]."""
+    [T, >= topk], out bf16 [T, h, 512], lse fp32 [T, h].  A 512-wide q (and
+    bf16 cache) selects the NoPE geometry."""
     T, h = int(q.shape[0]), int(q.shape[1])
     assert q.stride(2) == 1 and out.stride(2) == 1 and topk_idx.stride(1) == 1 and lse.stride(1) == 1
     logical = block_table is not None
@@ -174,7 +178,8 @@ def params_for(q, kv, topk_idx, out, lse, *, topk: int, scale: float, page_size:
         max_blocks_per_seq=int(block_table.shape[1]) if logical else 0,
         block_table_stride=int(block_table.stride(0)) if logical else 0,
         scale=scale, tiling=tiling, num_splits=num_splits, kernel_variant=kernel_variant,
-        gather_order=gather_order, q_strides=(int(q.stride(0)), int(q.stride(1))),
+        gather_order=gather_order, geometry="nope" if int(q.shape[2]) == D_V else "mla",
+        q_strides=(int(q.stride(0)), int(q.stride(1))),
         out_strides=(int(out.stride(0)), int(out.stride(1))),
         lse_stride=int(lse.stride(0)))
 

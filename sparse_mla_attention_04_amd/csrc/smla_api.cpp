@@ -31,10 +31,13 @@ int head_groups_for(const smla_params* p) {
   return 4;
 }
 
+int d_qk_of(const smla_params* p) { return p->geometry == SMLA_GEOM_NOPE ? SMLA_D_V : SMLA_D_QK; }
+
 // Parameter checks that need no pointers (and no device).
 int check_params(const smla_params* p) {
   if (!p) return SMLA_ERR_INVALID_ARG;
   if (p->kernel_variant < 0) return SMLA_ERR_INVALID_ARG;
+  if (p->geometry != SMLA_GEOM_MLA && p->geometry != SMLA_GEOM_NOPE) return SMLA_ERR_INVALID_ARG;
   if (p->gather_order < SMLA_GATHER_AUTO || p->gather_order > SMLA_GATHER_SLOT) return SMLA_ERR_INVALID_ARG;
   if (p->num_tokens < 0) return SMLA_ERR_INVALID_ARG;
   if (p->num_heads < 1) return SMLA_ERR_INVALID_ARG;
@@ -49,15 +52,16 @@ int check_params(const smla_params* p) {
       (p->kv_format == SMLA_KV_BF16 || p->kv_format == SMLA_KV_FP8_E4M3) &&
       p->tiling >= SMLA_TILING_AUTO && p->tiling <= SMLA_TILING_PAD64) {
     smla::FwdShape sh{};
-    if (!smla::fwd_shape(p->kv_format, head_groups_for(p), p->kernel_variant, &sh)) return SMLA_ERR_UNSUPPORTED;
+    if (!smla::fwd_shape(p->kv_format, head_groups_for(p), p->kernel_variant, p->geometry == SMLA_GEOM_NOPE, &sh))
+      return SMLA_ERR_UNSUPPORTED;
   }
   if (!std::isfinite(p->softmax_scale)) return SMLA_ERR_INVALID_ARG;
-  if (p->q_stride_h < SMLA_D_QK || p->q_stride_h % 8 || p->q_stride_t < 0 || p->q_stride_t % 8)
+  if (p->q_stride_h < d_qk_of(p) || p->q_stride_h % 8 || p->q_stride_t < 0 || p->q_stride_t % 8)
     return SMLA_ERR_INVALID_ARG;
   if (p->out_stride_h < SMLA_D_V || p->out_stride_h % 8 || p->out_stride_t < 0 || p->out_stride_t % 8)
     return SMLA_ERR_INVALID_ARG;
   if (p->lse_stride_t < 0) return SMLA_ERR_INVALID_ARG;
-  if (p->num_tokens > 1 && (p->q_stride_t < (int64_t)p->num_heads * p->q_stride_h - (p->q_stride_h - SMLA_D_QK) ||
+  if (p->num_tokens > 1 && (p->q_stride_t < (int64_t)p->num_heads * p->q_stride_h - (p->q_stride_h - d_qk_of(p)) ||
                             p->out_stride_t < (int64_t)p->num_heads * p->out_stride_h - (p->out_stride_h - SMLA_D_V) ||
                             p->lse_stride_t < p->num_heads))
     return SMLA_ERR_INVALID_ARG;   // rows of q / out / lse would overlap
@@ -103,7 +107,8 @@ int make_plan(const smla_params* p, int32_t num_cus, smla_plan* plan) {
   if (num_cus < 1) return SMLA_ERR_INVALID_ARG;
   smla::FwdShape sh{};
   const int hg = head_groups_for(p);
-  if (!smla::fwd_shape(p->kv_format, hg, p->kernel_variant, &sh)) return SMLA_ERR_UNSUPPORTED;
+  if (!smla::fwd_shape(p->kv_format, hg, p->kernel_variant, p->geometry == SMLA_GEOM_NOPE, &sh))
+    return SMLA_ERR_UNSUPPORTED;
   const int S = splits_for(p, num_cus, sh);
   smla_plan pl{};
   pl.head_groups = sh.head_groups;
@@ -242,7 +247,8 @@ int run(Mode mode, const smla_params* p, const void* q, const void* kv_cache, co
   a.bucket_shift = pl.gather_order == SMLA_GATHER_SLOT ? bucket_shift_for(a.num_slots) : -1;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (smla::launch_fwd(a, p->kv_format, pl.head_groups, p->kernel_variant, pl.grid, st) != hipSuccess)
+  if (smla::launch_fwd(a, p->kv_format, pl.head_groups, p->kernel_variant, p->geometry == SMLA_GEOM_NOPE, pl.grid,
+                       st) != hipSuccess)
     return SMLA_ERR_HIP;
   if (mode == Mode::kFull && pl.num_splits > 1) {
     smla::CombineArgs c{};

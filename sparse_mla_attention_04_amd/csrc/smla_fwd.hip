@@ -45,6 +45,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 constexpr int D_QK = 576;
 constexpr int D_V = 512;
 constexpr int ROW_BYTES = D_QK * 2;     // bf16 cache row
+constexpr int NOPE_ROW_BYTES = D_V * 2; // bf16 cache row of the NoPE geometry (no rope part)
 constexpr int FP8_ROW_BYTES = 640;      // fp8 cache row: 512 code bytes + 64 bf16 rope
 constexpr int FP8_SLOT_BYTES = 656;     // per-row share of an fp8 page (row + four fp32 scales)
 constexpr int LIST_CAP = 2048;          // index entries compacted per pass
@@ -53,7 +54,7 @@ constexpr float LN2 = 0.69314718055994530942f;
 constexpr float REF_HEADROOM = 64.0f;   // p = 2^(x - ref) may reach 2^64 before a second pass is forced
 
 template <int HG_, int NRG_, int RT_, int NST_, int FMT_, bool DSPLIT_ = false, bool PIPE_ = false,
-          bool PAIR_ = false, bool RSPLIT_ = false>
+          bool PAIR_ = false, bool RSPLIT_ = false, bool NOPE_ = false>
 struct Shape {
   static constexpr int HG = HG_;            // 16-head groups (waves per row group)
   static constexpr int NRG = NRG_;          // row groups (independent KV row streams)
@@ -65,7 +66,11 @@ struct Shape {
   static constexpr int NF = RT / 16;        // 16-row score fragments per tile
   static constexpr int NRH = RT / 8;        // 8-row DMA groups per tile
   static constexpr int RH_PER_WAVE = NRH / HG;
-  static constexpr int NLINES = FP8 ? FP8_ROW_BYTES / 128 : ROW_BYTES / 128;   // 128-B lines per row
+  // NOPE: the NoPE geometry, rows and queries of the 512 latent dims only
+  static constexpr bool NOPE = NOPE_;
+  static constexpr int ROWB = FP8 ? FP8_ROW_BYTES : NOPE ? NOPE_ROW_BYTES : ROW_BYTES;  // bytes per cache row
+  static constexpr int KS = NOPE ? 16 : 18;           // 32-dim k-steps of a score
+  static constexpr int NLINES = ROWB / 128;           // 128-B lines per row
   static constexpr int BODY_BYTES = RT * NLINES * 128;
   static constexpr int TILE_BYTES = BODY_BYTES + (FP8 ? RT * 16 : 0);       // + fp32 block scales
   static constexpr int PER = NLINES * RH_PER_WAVE + (FP8 ? 1 : 0);  // DMA instructions per wave per tile
@@ -115,7 +120,8 @@ struct Shape {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(LIST_CAP % NTHR == 0, "compaction split");
   static_assert(!DSPLIT || (HG == 4 && NRG == 1 && RT == 32 && !FP8), "output-dim split layout");
-  static_assert(!PIPE || (DSPLIT && NST >= 3 && PER == 9), "pipelined variant layout");
+  static_assert(!PIPE || (DSPLIT && NST >= 3 && PER == NLINES), "pipelined variant layout");
+  static_assert(!NOPE || !FP8, "the NoPE geometry is built for bf16 caches");
   static_assert(!DSPLIT || PIPE, "the output-dim split runs in the pipelined schedule");
   static_assert(!PAIR || (FP8 && HG == 2 && RT == 32 && !DSPLIT), "row/dim-split pair layout");
   static_assert(!RSPLIT || PIPE, "the row-half score split runs in the pipelined schedule");
@@ -180,14 +186,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
 
 // Byte offset of a cache row: bf16 rows are contiguous; fp8 pages hold the
 // page's rows first ([512 codes | 64 bf16 rope] each) and then their scales.
-template <bool FP8>
+template <bool FP8, int ROWB>
 __device__ __forceinline__ int64_t row_offset(const FwdArgs& a, int slot) {
   if constexpr (FP8) {
     const int64_t page = slot >> a.page_shift;
     const int64_t rin = slot & ((1 << a.page_shift) - 1);
     return page * ((int64_t)FP8_SLOT_BYTES << a.page_shift) + rin * FP8_ROW_BYTES;
   } else {
-    return (int64_t)slot * ROW_BYTES;
+    return (int64_t)slot * ROWB;
   }
 }
 
@@ -439,7 +445,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
     if (head < a.h) {
       const uint16_t* qp = a.q + (int64_t)t * a.q_st + (int64_t)head * a.q_sh + 8 * g4;
 #pragma unroll
-      for (int kk = 0; kk < 18; ++kk) {
+      for (int kk = 0; kk < S::KS; ++kk) {
         // fp8 latent k-steps take their dims in the order the 16-byte code reads
         // deliver them: step (block b, s) of a lane covers dims
         // 128b + 64(s >> 1) + 16*g4 + 8(s & 1) .. +7 (a permutation of the block's
@@ -451,7 +457,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
       }
     } else {
 #pragma unroll
-      for (int kk = 0; kk < 18; ++kk) qb[18 * e + kk] = bf16x8{};
+      for (int kk = 0; kk < S::KS; ++kk) qb[18 * e + kk] = bf16x8{};
     }
   }
 
@@ -490,7 +496,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         li = (li < n_valid) ? li : n_valid - 1;           // tail rows repeat the last valid row
         const int slot = list[li];
         const int q = (lane & 7) ^ swz<S::FP8>(r);
-        const uint8_t* g = a.kv + row_offset<S::FP8>(a, slot) + q * 16;
+        const uint8_t* g = a.kv + row_offset<S::FP8, S::ROWB>(a, slot) + q * 16;
         const uint32_t mb = tl + (uint32_t)rh * 1024u;
         // line L of the row lands at tile position L*RT*8 + rh*64 + lane
         dma16<0 * 128>(g, mb + 0 * (S::RT * 128 - 128));
@@ -502,7 +508,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
           dma16<5 * 128>(g, mb + 5 * (S::RT * 128 - 128));
           dma16<6 * 128>(g, mb + 6 * (S::RT * 128 - 128));
           dma16<7 * 128>(g, mb + 7 * (S::RT * 128 - 128));
-          dma16<8 * 128>(g, mb + 8 * (S::RT * 128 - 128));
+          if constexpr (S::NLINES > 8) dma16<8 * 128>(g, mb + 8 * (S::RT * 128 - 128));
         }
       }
       if constexpr (S::FP8) {
@@ -582,9 +588,9 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
       for (int f = 0; f < S::NF; ++f) {
         // all 18 K operands of the fragment are requested before its first
         // MFMA, so the LDS latency is paid once per fragment
-        bf16x8 kb[18];
+        bf16x8 kb[S::KS];
 #pragma unroll
-        for (int kk = 0; kk < 18; ++kk)
+        for (int kk = 0; kk < S::KS; ++kk)
           kb[kk] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[f][kk & 1] + (kk >> 1) * S::RT * 128);
         __builtin_amdgcn_sched_barrier(0);
         // six independent accumulation chains: a dependent MFMA waits for its
@@ -593,7 +599,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
 #pragma unroll
         for (int c = 0; c < 6; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < 18; ++kk)
+        for (int kk = 0; kk < S::KS; ++kk)
           acc[kk % 6] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qb[kk], acc[kk % 6], 0, 0, 0);
         sc[f] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + (acc[4] + acc[5]);
       }
@@ -816,7 +822,9 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
 
     // the compiler's wait for the query loads lands here, before any gather is in flight
 #pragma unroll
-    for (int kk = 0; kk < 18 * S::NE; ++kk) asm volatile("" : : "v"(qb[kk]));
+    for (int e = 0; e < S::NE; ++e)
+#pragma unroll
+      for (int kk = 0; kk < S::KS; ++kk) asm volatile("" : : "v"(qb[18 * e + kk]));
 
     if constexpr (S::PIPE) {
       // ---- software-pipelined schedule (one tile stream, four waves):
@@ -837,7 +845,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         int li = itd * S::RT + r;
         li = (li < n_valid) ? li : n_valid - 1;
         const int slot = list[li];
-        dg = a.kv + (int64_t)slot * ROW_BYTES + ((lane & 7) ^ swz<S::FP8>(r)) * 16;
+        dg = a.kv + (int64_t)slot * S::ROWB + ((lane & 7) ^ swz<S::FP8>(r)) * 16;
         dmb = tile_lds(itd) + (uint32_t)hg * 1024u;
       };
       auto dma_line = [&](int L) {
@@ -920,7 +928,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
           // k-step kk's K operand (this wave's 16 rows) feeds the MFMAs of both
           // head groups; chain (group, kk mod 2) is fed every 4th MFMA
           constexpr int KR = 4;
-          bf16x8 kr[18];
+          bf16x8 kr[S::KS];
 #pragma unroll
           for (int i = 0; i < KR; ++i)
             kr[i] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + krs[i & 1] + (i >> 1) * S::RT * 128);
@@ -929,14 +937,14 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
 #pragma unroll
           for (int e = 0; e < 2; ++e) acc[e][0] = acc[e][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kk = 0; kk < 18; ++kk) {
+          for (int kk = 0; kk < S::KS; ++kk) {
 #pragma unroll
             for (int e = 0; e < 2; ++e)
               acc[e][kk & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[kk], qb[18 * e + kk], acc[e][kk & 1], 0, 0, 0);
             const int j = kk + KR;
-            if (j < 18) kr[j] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + krs[j & 1] + (j >> 1) * S::RT * 128);
+            if (j < S::KS) kr[j] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + krs[j & 1] + (j >> 1) * S::RT * 128);
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            if (j < 18) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (j < S::KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
 #pragma unroll
           for (int e = 0; e < 2; ++e) out[e] = acc[e][0] + acc[e][1];
@@ -945,7 +953,8 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         // MFMA i is (fragment i & 1, k-step i >> 1); it accumulates into chain
         // (fragment, k-step mod 4), so each of the 8 chains is fed every 8th MFMA
         // and no MFMA waits for its predecessor's result
-        bf16x8 kr[36];
+        constexpr int NM = 2 * S::KS;   // score MFMAs of a tile
+        bf16x8 kr[NM];
 #pragma unroll
         for (int i = 0; i < KRING; ++i)
           kr[i] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[i & 1][(i >> 1) & 1] + (i >> 2) * S::RT * 128);
@@ -956,15 +965,15 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
 #pragma unroll
           for (int c = 0; c < 4; ++c) acc[f][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 36; ++i) {
+        for (int i = 0; i < NM; ++i) {
           const int f = i & 1, kk = i >> 1;
           acc[f][kk & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[i], qb[kk], acc[f][kk & 3], 0, 0, 0);
           const int j = i + KRING;
-          if (j < 36)
+          if (j < NM)
             kr[j] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[j & 1][(j >> 1) & 1] + (j >> 2) * S::RT * 128);
           // one MFMA, then its ring read
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (j < 36) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if (j < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
 #pragma unroll
         for (int f = 0; f < 2; ++f) out[f] = (acc[f][0] + acc[f][1]) + (acc[f][2] + acc[f][3]);
@@ -984,7 +993,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         for (int st = 0; st < S::NST; ++st) {
           dma_prep(st);
 #pragma unroll
-          for (int L = 0; L < 9; ++L) dma_line(L);
+          for (int L = 0; L < S::NLINES; ++L) dma_line(L);
         }
         wait_vm<(S::NST - 1) * S::PER>();
         lds_barrier();
@@ -1040,7 +1049,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
             vpre[f] = read_vt(it + 1, f);
             dma_line(f);
           }
-          dma_line(8);
+          if constexpr (S::NLINES > 8) dma_line(8);
           publish(pb, (it + 1) & 1);
         }
       }
@@ -1285,6 +1294,10 @@ using V_H2_B = Shape<2, 1, 32, 4, 0>;
 using V_H4_A = Shape<4, 1, 32, 4, 0, true, true>;
 using V_H4_B = Shape<4, 1, 32, 4, 0>;
 using V_H4_C = Shape<4, 1, 32, 4, 0, true, true, false, true>;
+// NoPE geometry (bf16, 512-wide rows): the default shapes
+using N_H1_A = Shape<1, 4, 16, 2, 0, false, false, false, false, true>;
+using N_H2_A = Shape<2, 2, 32, 2, 0, false, false, false, false, true>;
+using N_H4_A = Shape<4, 1, 32, 4, 0, true, true, false, false, true>;
 using F_H1_A = Shape<2, 2, 32, 3, 1, false, false, true>;
 using F_H1_B = Shape<1, 2, 32, 3, 1>;
 using F_H2_A = Shape<2, 1, 32, 4, 1>;
@@ -1303,7 +1316,16 @@ hipError_t launch_one(const FwdArgs& a, int64_t grid, hipStream_t stream) {
 
 }  // namespace
 
-bool fwd_shape(int kv_format, int head_groups, int variant, FwdShape* shape) {
+bool fwd_shape(int kv_format, int head_groups, int variant, int nope, FwdShape* shape) {
+  if (nope) {
+    if (kv_format != 0 || variant != 0) return false;
+    switch (head_groups) {
+      case 1: *shape = shape_of<N_H1_A>(); return true;
+      case 2: *shape = shape_of<N_H2_A>(); return true;
+      case 4: *shape = shape_of<N_H4_A>(); return true;
+      default: return false;
+    }
+  }
   if (kv_format == 1) {
     if (variant != 0 && !(variant == 1 && head_groups == 1)) return false;
     switch (head_groups) {
@@ -1323,8 +1345,16 @@ bool fwd_shape(int kv_format, int head_groups, int variant, FwdShape* shape) {
   }
 }
 
-hipError_t launch_fwd(const FwdArgs& a, int kv_format, int head_groups, int variant, int64_t grid,
+hipError_t launch_fwd(const FwdArgs& a, int kv_format, int head_groups, int variant, int nope, int64_t grid,
                       hipStream_t stream) {
+  if (nope) {
+    switch (head_groups) {
+      case 1: return launch_one<N_H1_A>(a, grid, stream);
+      case 2: return launch_one<N_H2_A>(a, grid, stream);
+      case 4: return launch_one<N_H4_A>(a, grid, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   if (kv_format == 1) {
     switch (head_groups) {
       case 1: return variant == 1 ? launch_one<F_H1_B>(a, grid, stream) : launch_one<F_H1_A>(a, grid, stream);

@@ -43,10 +43,10 @@ struct FwdShape {
 };
 
 // Shape of kernel `variant` for `head_groups`; returns false when no such kernel exists.
-bool fwd_shape(int kv_format, int head_groups, int variant, FwdShape* shape);
+bool fwd_shape(int kv_format, int head_groups, int variant, int nope, FwdShape* shape);
 
 // Launches; return a hipError_t.
-hipError_t launch_fwd(const FwdArgs& a, int kv_format, int head_groups, int variant, int64_t grid,
+hipError_t launch_fwd(const FwdArgs& a, int kv_format, int head_groups, int variant, int nope, int64_t grid,
                       hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 

@@ -71,10 +71,28 @@ def test_zero_tokens_is_noop():
     (dict(kernel_variant=2, kv_format="fp8"), B.SMLA_ERR_UNSUPPORTED),
     (dict(kernel_variant=2), B.SMLA_ERR_UNSUPPORTED),                 # h = 8: no third shape
     (dict(kernel_variant=3, num_heads=64), B.SMLA_ERR_UNSUPPORTED),
+    (dict(geometry="nope", kv_format="fp8"), B.SMLA_ERR_UNSUPPORTED),     # NoPE: bf16 caches only
+    (dict(geometry="nope", kernel_variant=1), B.SMLA_ERR_UNSUPPORTED),    # NoPE: default shapes only
+    (dict(geometry="mla", q_strides=(8 * 512, 512)), B.SMLA_ERR_INVALID_ARG),   # 576-wide heads
+    (dict(geometry="nope", q_strides=(8 * 512, 504)), B.SMLA_ERR_INVALID_ARG),
 ])
 def test_bad_params_rejected(kw, code):
     assert _fwd(_params(**kw)) == code
     assert B.workspace_size(_params(**kw)) == 0
+
+
+def test_geometry_values():
+    p = _params()
+    p.geometry = 2
+    assert _fwd(p) == B.SMLA_ERR_INVALID_ARG
+    # NoPE with 512-wide query heads is a valid request (fake pointers, so the
+    # call stops at the device query or launch, never at validation)
+    for h in (8, 24, 64):
+        pn = _params(geometry="nope", num_heads=h)
+        assert pn.q_stride_h == 512
+        pl = B.plan(pn, num_cus=256)
+        assert pl.head_groups == (1 if h <= 16 else 2 if h <= 32 else 4)
+        assert B.workspace_size(pn) == B.workspace_size(_params(num_heads=h))
 
 
 def test_bad_gather_order_rejected():

@@ -542,3 +542,55 @@ def test_auto_gather_order_on_prefill_batch():
     out, lse = to_np(*run_gpu(dev))
     rows = np.unique(np.r_[np.arange(0, c.num_tokens, 97), c.num_tokens - 1])
     check(out[rows], lse[rows], *oracle(c, rows=rows), what="c3 h8 slot order")
+
+
+# --------------------------------------------------------------------------- NoPE geometry
+
+@pytest.mark.parametrize("h,tiling,splits", [(8, "native", 0), (12, "native", 0), (16, "native", 3),
+                                             (24, "native", 0), (32, "native", 0), (48, "native", 0),
+                                             (64, "native", 0), (64, "native", 4), (8, "pad64", 0)])
+def test_nope_mini(h, tiling, splits):
+    """512-wide query heads and cache rows (no rope part) against the oracle."""
+    say("nope mini", h, tiling, splits)
+    c = G.make_mini(seed=71, num_heads=h, topk=300, rope_dims=0)
+    out, lse = to_np(*run_gpu(Dev(c), tiling=tiling, num_splits=splits))
+    check(out, lse, *oracle(c), what="nope h=%d %s s%d" % (h, tiling, splits))
+
+
+def test_nope_slot_mode_and_orders_bit_identical():
+    """SLOT indices give the same bits as LOGICAL ones, and (unsplit) the list
+    and slot gather orders agree with the oracle."""
+    say("nope slot mode / gather orders")
+    c = G.make_mini(seed=72, num_heads=64, topk=300, num_seqs=24, tokens_per_seq=30, rope_dims=0)
+    dev = Dev(c)
+    o1, l1 = to_np(*run_gpu(dev, num_splits=1))
+    dev_s = Dev(c, idx=slot_indices(c))
+    o2, l2 = to_np(*run_gpu(dev_s, logical=False, num_splits=1))
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    ref = oracle(c)
+    check(o1, l1, *ref, what="nope h64 many rows")
+    for order in ("list", "slot"):
+        o, l = to_np(*run_gpu(dev, num_splits=1, gather_order=order))
+        check(o, l, *ref, what="nope h64 %s" % order)
+
+
+def test_nope_recompute_and_two_chunks():
+    say("nope recompute / two chunks")
+    c = G.make_mini(seed=73, num_heads=16, topk=300, drop_frac=0.0, rope_dims=0)
+    kv = c.kv.copy()
+    flat = kv.reshape(-1, 512)
+    hot = 9
+    qsign = np.sign((c.q[0, 0].astype(np.uint32) << 16).view(np.float32))
+    flat[hot] = G.to_bf16_bits((16.0 * qsign).astype(np.float32))
+    c2 = G.Case(**{**c.__dict__, "kv": kv})
+    sidx = slot_indices(c2)
+    sidx[:, -1] = hot
+    from oracle import sparse_mla_oracle as O
+    ro, rl = O.sparse_mla_forward(c2.q, c2.kv, sidx, topk=c2.topk, scale=c2.scale, index_mode="slot")
+    for splits in (1, 3):
+        out, lse = to_np(*run_gpu(Dev(c2, idx=sidx), logical=False, num_splits=splits))
+        check(out, lse, ro, rl, "nope spread s%d" % splits)
+    c = G.build_case("nope_two_chunks", seed=74, hist=[6000], new=[40], num_heads=64, topk=2100,
+                     drop_frac=0.05, rope_dims=0)
+    out, lse = to_np(*run_gpu(Dev(c), num_splits=1))
+    check(out, lse, *oracle(c), what="nope topk 2100")
