@@ -235,6 +235,29 @@ int sparse_mla_lse_combine(const float* part_out, const float* part_lse, int32_t
                            int32_t num_splits, int32_t num_heads, void* out, int64_t out_stride_t,
                            int64_t out_stride_h, float* lse, int64_t lse_stride_t, void* stream);
 
+/* Dense causal fallback: every query row t attends to all positions
+ * 0 .. positions[t] of its sequence -- the same result as sparse_mla_fwd with
+ * the index list 0, 1, .., positions[t] (prhub report on vLLM PR #55738,
+ * "Motivation": a prefix no longer than top-k is better served densely,
+ * about 1.6 ms per layer through the top-k kernel against 0.2 ms dense for
+ * 8 x 2048 tokens).  A work-group takes up to 64 / h consecutive query rows
+ * of one sequence and gathers each cache row once for all of them.
+ *   query_start int32 [num_seqs + 1] (device): rows of sequence s are
+ *               [query_start[s], query_start[s + 1]) -- nondecreasing, first
+ *               0, last num_tokens (a varlen "cu_seqlens" layout)
+ *   positions   int32 [num_tokens] (device): the causal position of each row
+ *   block_table as for SMLA_IDX_LOGICAL (positions past the table, or blocks
+ *               whose page is outside the pool, are skipped like -1 entries)
+ * Requirements (else SMLA_ERR_UNSUPPORTED): kv_format bf16, index_mode
+ * SMLA_IDX_LOGICAL, page_size >= 16, max_blocks_per_seq and num_seqs at most
+ * 2048, num_splits 0 or 1, tiling AUTO / NATIVE, kernel_variant 0.
+ * topk / idx_stride must be valid but are not used; geometry may be MLA or
+ * NOPE.  Other validation, ownership and error behaviour as sparse_mla_fwd;
+ * no workspace. */
+int sparse_mla_dense_fwd(const smla_params* p, const void* q, const void* kv_cache,
+                         const int32_t* block_table, const int32_t* query_start,
+                         const int32_t* positions, void* out, float* lse, void* stream);
+
 /* Static, human-readable text for a status code. */
 const char* sparse_mla_status_string(int status);
 

@@ -31,7 +31,7 @@ D_QK, D_V = 576, 512
 
 EXPORTS = ("sparse_mla_workspace_size", "sparse_mla_plan", "sparse_mla_plan_for",
            "sparse_mla_fwd", "sparse_mla_fwd_partials", "sparse_mla_lse_combine",
-           "sparse_mla_status_string")
+           "sparse_mla_status_string", "sparse_mla_dense_fwd")
 
 
 class Params(ctypes.Structure):
@@ -99,6 +99,8 @@ def lib() -> ctypes.CDLL:
                                              ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                              ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         L.sparse_mla_lse_combine.restype = ctypes.c_int
+        L.sparse_mla_dense_fwd.argtypes = [ctypes.POINTER(Params)] + [ctypes.c_void_p] * 8
+        L.sparse_mla_dense_fwd.restype = ctypes.c_int
         L.sparse_mla_status_string.argtypes = [ctypes.c_int]
         L.sparse_mla_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -200,6 +202,29 @@ def fwd(q, kv, topk_idx, out, lse, *, topk: int, scale: float, workspace=None, p
                               ctypes.c_void_p(int(stream)))
     if rc != SMLA_OK:
         raise SparseMLAError(rc, "sparse_mla_fwd")
+
+
+def dense_fwd(q, kv, out, lse, *, block_table, query_start, positions, scale: float, page_size: int = 64,
+              stream=None) -> None:
+    """sparse_mla_dense_fwd on torch tensors: row t of sequence s (rows
+    query_start[s] .. query_start[s+1]-1) attends to positions 0 .. positions[t]
+    of its sequence through the block table.  q bf16 [T, h, 576] (or 512 for the
+    NoPE geometry), kv bf16 [pages, P, same], out bf16 [T, h, 512], lse fp32 [T, h]."""
+    import torch
+    T, h = int(q.shape[0]), int(q.shape[1])
+    assert q.stride(2) == 1 and out.stride(2) == 1 and lse.stride(1) == 1
+    p = make_params(num_tokens=T, num_heads=h, topk=1, page_size=page_size, num_pages=int(kv.shape[0]),
+                    index_mode="logical", num_seqs=int(query_start.shape[0]) - 1,
+                    max_blocks_per_seq=int(block_table.shape[1]), block_table_stride=int(block_table.stride(0)),
+                    scale=scale, num_splits=1, geometry="nope" if int(q.shape[2]) == D_V else "mla",
+                    q_strides=(int(q.stride(0)), int(q.stride(1))), out_strides=(int(out.stride(0)), int(out.stride(1))),
+                    lse_stride=int(lse.stride(0)))
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    rc = lib().sparse_mla_dense_fwd(ctypes.byref(p), _ptr(q), _ptr(kv), _ptr(block_table), _ptr(query_start),
+                                    _ptr(positions), _ptr(out), _ptr(lse), ctypes.c_void_p(int(stream)))
+    if rc != SMLA_OK:
+        raise SparseMLAError(rc, "sparse_mla_dense_fwd")
 
 
 def fwd_partials(q, kv, topk_idx, workspace, *, topk: int, scale: float, page_size: int = 64,

@@ -312,6 +312,63 @@ int sparse_mla_lse_combine(const float* part_out, const float* part_lse, int32_t
   return SMLA_OK;
 }
 
+int sparse_mla_dense_fwd(const smla_params* p, const void* q, const void* kv_cache, const int32_t* block_table,
+                         const int32_t* query_start, const int32_t* positions, void* out, float* lse,
+                         void* stream) {
+  int rc = check_params(p);
+  if (rc != SMLA_OK) return rc;
+  if (p->kv_format != SMLA_KV_BF16 || p->index_mode != SMLA_IDX_LOGICAL || p->page_size < 16 ||
+      p->max_blocks_per_seq > smla::kListCap || p->num_seqs > smla::kListCap || p->num_splits > 1 ||
+      p->tiling == SMLA_TILING_PAD64 || p->kernel_variant != 0)
+    return SMLA_ERR_UNSUPPORTED;
+  if (p->num_tokens == 0) return SMLA_OK;
+  if (!q || !kv_cache || !block_table || !query_start || !positions || !out || !lse) return SMLA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(block_table, 4) || !aligned(query_start, 4) ||
+      !aligned(positions, 4) || !aligned(out, 16) || !aligned(lse, 4))
+    return SMLA_ERR_INVALID_ARG;
+  int32_t cus = 0;
+  rc = device_cus(&cus);
+  if (rc != SMLA_OK) return rc;
+  (void)cus;
+  const int qb = SMLA_MAX_HEADS / p->num_heads;
+  // blocks: sum over sequences of ceil(n_s / qb) <= ceil(T / qb) + num_seqs
+  const int64_t units = ((int64_t)p->num_tokens + qb - 1) / qb + p->num_seqs;
+  smla::FwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv = static_cast<const uint8_t*>(kv_cache);
+  a.block_table = block_table;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.q_st = p->q_stride_t;
+  a.q_sh = p->q_stride_h;
+  a.out_st = p->out_stride_t;
+  a.out_sh = p->out_stride_h;
+  a.lse_st = p->lse_stride_t;
+  a.bt_stride = p->block_table_stride;
+  a.num_slots = p->num_pages * p->page_size;
+  a.num_pages = p->num_pages;
+  a.units = units;
+  a.T = p->num_tokens;
+  a.h = p->num_heads;
+  a.topk = 1;
+  a.num_splits = 1;
+  a.page_shift = log2i(p->page_size);
+  a.index_mode = SMLA_IDX_LOGICAL;
+  a.num_seqs = p->num_seqs;
+  a.max_blocks = p->max_blocks_per_seq;
+  a.grid_per_xcd = (int32_t)((units + 7) / 8);
+  a.write_partials = 0;
+  a.scale_log2 = p->softmax_scale * 1.44269504088896340736f;
+  a.bucket_shift = -1;
+  a.query_start = query_start;
+  a.positions = positions;
+  a.dense_qb = qb;
+  if (smla::launch_dense(a, p->geometry == SMLA_GEOM_NOPE, (units + 7) / 8 * 8, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return SMLA_ERR_HIP;
+  return SMLA_OK;
+}
+
 const char* sparse_mla_status_string(int status) {
   switch (status) {
     case SMLA_OK: return "ok";

@@ -48,13 +48,13 @@ constexpr int ROW_BYTES = D_QK * 2;     // bf16 cache row
 constexpr int NOPE_ROW_BYTES = D_V * 2; // bf16 cache row of the NoPE geometry (no rope part)
 constexpr int FP8_ROW_BYTES = 640;      // fp8 cache row: 512 code bytes + 64 bf16 rope
 constexpr int FP8_SLOT_BYTES = 656;     // per-row share of an fp8 page (row + four fp32 scales)
-constexpr int LIST_CAP = 2048;          // index entries compacted per pass
+constexpr int LIST_CAP = kListCap;      // index entries compacted per pass
 constexpr float NEG_INF = -__builtin_inff();
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float REF_HEADROOM = 64.0f;   // p = 2^(x - ref) may reach 2^64 before a second pass is forced
 
 template <int HG_, int NRG_, int RT_, int NST_, int FMT_, bool DSPLIT_ = false, bool PIPE_ = false,
-          bool PAIR_ = false, bool RSPLIT_ = false, bool NOPE_ = false>
+          bool PAIR_ = false, bool RSPLIT_ = false, bool NOPE_ = false, bool DENSE_ = false>
 struct Shape {
   static constexpr int HG = HG_;            // 16-head groups (waves per row group)
   static constexpr int NRG = NRG_;          // row groups (independent KV row streams)
@@ -122,6 +122,14 @@ struct Shape {
   static_assert(!DSPLIT || (HG == 4 && NRG == 1 && RT == 32 && !FP8), "output-dim split layout");
   static_assert(!PIPE || (DSPLIT && NST >= 3 && PER == NLINES), "pipelined variant layout");
   static_assert(!NOPE || !FP8, "the NoPE geometry is built for bf16 caches");
+  // DENSE (with PIPE): dense causal mode.  A work-group takes a block of up to
+  // 64 / h consecutive query rows of one sequence; its 64 query slots are
+  // (row, head) pairs m = row * h + head, and every cache row of positions
+  // 0 .. max position is gathered once for all of them (tile i = positions
+  // 32i .. 32i + 31 through the block table), each slot masking positions
+  // past its own row's.
+  static constexpr bool DENSE = DENSE_;
+  static_assert(!DENSE || (PIPE && !RSPLIT && !FP8), "dense mode runs the pipelined bf16 schedule");
   static_assert(!DSPLIT || PIPE, "the output-dim split runs in the pipelined schedule");
   static_assert(!PAIR || (FP8 && HG == 2 && RT == 32 && !DSPLIT), "row/dim-split pair layout");
   static_assert(!RSPLIT || PIPE, "the row-half score split runs in the pipelined schedule");
@@ -369,6 +377,55 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
   const int hg = wave % S::HG, rg = wave / S::HG;
   const int g4 = lane >> 4, n = lane & 15;
 
+  // ---- dense mode: block `unit` -> (sequence, first row, rows).  Sequence s
+  // has ceil(n_s / qb) blocks; wave 0 scans the block counts 64 sequences at
+  // a time and the lane owning `unit` publishes it through LDS.
+  int d_seq = 0, d_r0 = 0, d_nr = 0;
+  if constexpr (S::DENSE) {
+    const int qb = a.dense_qb;
+    int* found = reinterpret_cast<int*>(smem + S::CNT_OFF);
+    if (tid == 0) found[0] = -1;
+    __syncthreads();
+    if (wave == 0) {
+      int64_t base = 0;
+      for (int c = 0; c < a.num_seqs; c += 64) {
+        const int s_ = c + lane;
+        int q0 = 0, q1 = 0;
+        if (s_ < a.num_seqs) {
+          q0 = a.query_start[s_];
+          q1 = a.query_start[s_ + 1];
+        }
+        const int nb = (q1 > q0) ? (q1 - q0 + qb - 1) / qb : 0;
+        int incl = nb;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int v = __shfl_up(incl, d, 64);
+          if (lane >= d) incl += v;
+        }
+        const int64_t lo = base + incl - nb, hi = base + incl;
+        if (unit >= lo && unit < hi) {
+          const int r0 = q0 + (int)(unit - lo) * qb;
+          found[0] = s_;
+          found[1] = r0;
+          found[2] = (q1 - r0 < qb) ? q1 - r0 : qb;
+        }
+        base += __shfl(incl, 63, 64);
+        if (base > unit) break;
+      }
+    }
+    __syncthreads();
+    d_seq = found[0];
+    d_r0 = found[1];
+    d_nr = found[2];
+    __syncthreads();
+    if (d_seq < 0) return;   // past the last block (the grid is an upper bound)
+  }
+  // dense mode: this lane's query slot m = 16 * hg + n as (row, head); slots
+  // past the block's rows repeat its last row (computed, never written)
+  const int d_m = 16 * hg + n;
+  const int d_row = S::DENSE ? (d_m / a.h < d_nr ? d_m / a.h : d_nr - 1) : 0;
+  const int d_head = S::DENSE ? d_m - (d_m / a.h) * a.h : 0;
+
   // ---- per-lane LDS offsets inside a tile
   // tile layout: position(r, c) = (c / 8) * RT * 8 + r * 8 + ((c % 8) ^ swz(r)), 16 B each
   uint32_t kofs[S::NF][2];     // K operand: row 16f+n, chunk 4*kk+g4
@@ -434,7 +491,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
       raw[i] = (e < ce) ? idx_row[e] : -1;
     }
   };
-  load_raw(c0, (c0 + LIST_CAP < c1) ? c0 + LIST_CAP : c1);
+  if constexpr (!S::DENSE) load_raw(c0, (c0 + LIST_CAP < c1) ? c0 + LIST_CAP : c1);
 
   // ---- queries of this wave's 16 heads, in the MFMA B-operand layout:
   //      lane (g4, n) holds head hg*16+n, dims 32*kk + 8*g4 .. +7
@@ -442,8 +499,9 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
 #pragma unroll
   for (int e = 0; e < S::NE; ++e) {
     const int head = (S::RSPLIT ? 32 * (wave >> 1) + 16 * e : (S::PAIR ? 0 : hg) * 16) + n;
-    if (head < a.h) {
-      const uint16_t* qp = a.q + (int64_t)t * a.q_st + (int64_t)head * a.q_sh + 8 * g4;
+    if (S::DENSE || head < a.h) {
+      const uint16_t* qp = S::DENSE ? a.q + (int64_t)(d_r0 + d_row) * a.q_st + (int64_t)d_head * a.q_sh + 8 * g4
+                                    : a.q + (int64_t)t * a.q_st + (int64_t)head * a.q_sh + 8 * g4;
 #pragma unroll
       for (int kk = 0; kk < S::KS; ++kk) {
         // fp8 latent k-steps take their dims in the order the 16-byte code reads
@@ -465,17 +523,53 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
   // queries so its latency overlaps theirs
   int seq_ok = 1;
   int64_t bt_row = 0;
-  if (a.index_mode == 1) {
+  if constexpr (S::DENSE) {
+    bt_row = (int64_t)d_seq * a.bt_stride;
+  } else if (a.index_mode == 1) {
     const int seq = a.token_seq[t];
     seq_ok = (seq >= 0 && seq < a.num_seqs);
     bt_row = seq_ok ? (int64_t)seq * a.bt_stride : 0;
+  }
+  // dense mode: this slot's causal limit, and the block's largest one
+  int d_plim = 0;
+  if constexpr (S::DENSE) {
+    const int lastpos = a.max_blocks * (1 << a.page_shift) - 1;   // beyond the block table: skipped
+    int pl = a.positions[d_r0 + d_row];
+    pl = pl < lastpos ? pl : lastpos;
+    d_plim = pl;
   }
 
   for (int pass = 0; pass < 2; ++pass) {
   for (int64_t cs = c0; cs < c1; cs += LIST_CAP) {
     const int64_t ce = (cs + LIST_CAP < c1) ? cs + LIST_CAP : c1;
-    if (cs != c0 || pass != 0) load_raw(cs, ce);
-    const int n_valid = compact_chunk<S::NW, S::EPT>(a, raw, seq_ok, bt_row, list, wcnt, wave, lane);
+    int n_valid;
+    if constexpr (S::DENSE) {
+      // positions 0 .. the block's largest limit; list[i] = the block-table
+      // page of block i (-1 when invalid: those positions are skipped)
+      float pm = (float)d_plim;
+      pm = max_xor16_32(pm);
+      pm = fmaxf(pm, wave_xor(pm, 1));
+      pm = fmaxf(pm, wave_xor(pm, 2));
+      pm = fmaxf(pm, wave_xor(pm, 4));
+      pm = fmaxf(pm, wave_xor(pm, 8));
+      float* wmax = reinterpret_cast<float*>(smem + S::CNT_OFF);
+      if (lane == 0) wmax[wave] = pm;
+      __syncthreads();
+      float bm = wmax[0];
+#pragma unroll
+      for (int w = 1; w < S::NW; ++w) bm = fmaxf(bm, wmax[w]);
+      const int pmax = (int)bm;
+      const int npg = (pmax >> a.page_shift) + 1;
+      for (int i = tid; i < npg; i += S::NTHR) {
+        const int pg = a.block_table[bt_row + i];
+        list[i] = (pg >= 0 && pg < a.num_pages) ? pg : -1;
+      }
+      __syncthreads();
+      n_valid = pmax + 1;
+    } else {
+      if (cs != c0 || pass != 0) load_raw(cs, ce);
+      n_valid = compact_chunk<S::NW, S::EPT>(a, raw, seq_ok, bt_row, list, wcnt, wave, lane);
+    }
 
     // ---- tiles: tile i belongs to row group i % NRG
     const int ntile = (n_valid + S::RT - 1) / S::RT;
@@ -844,7 +938,14 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         const int r = 8 * hg + (lane >> 3);
         int li = itd * S::RT + r;
         li = (li < n_valid) ? li : n_valid - 1;
-        const int slot = list[li];
+        int slot;
+        if constexpr (S::DENSE) {
+          // position li of the sequence (an invalid page reads page 0; masked)
+          const int pg = list[li >> a.page_shift];
+          slot = ((pg < 0 ? 0 : pg) << a.page_shift) | (li & ((1 << a.page_shift) - 1));
+        } else {
+          slot = list[li];
+        }
         dg = a.kv + (int64_t)slot * S::ROWB + ((lane & 7) ^ swz<S::FP8>(r)) * 16;
         dmb = tile_lds(itd) + (uint32_t)hg * 1024u;
       };
@@ -872,6 +973,16 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
       // row halves, exchanged with the partner wave through LDS.
       auto softmax = [&](int it, const f32x4* scv, bool first) -> bf16x8 {
         const int left = n_valid - it * S::RT;
+        // dense mode: positions past the slot's own row, or on an invalid
+        // page (pages hold >= 16 rows, so a 16-row fragment has one page)
+        bool pgok[2] = {true, true};
+        if constexpr (S::DENSE) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int p0 = it * S::RT + 16 * q;
+            pgok[q] = p0 < n_valid && list[p0 >> a.page_shift] >= 0;
+          }
+        }
         float x[2][4];
         float mx[2] = {NEG_INF, NEG_INF};
 #pragma unroll
@@ -880,7 +991,8 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
           for (int j = 0; j < 4; ++j) {
             const int row = (S::RSPLIT ? 16 * (wave & 1) : 16 * q) + 4 * g4 + j;
             const float v = scv[q][j] * a.scale_log2;
-            x[q][j] = (row < left) ? v : NEG_INF;
+            const bool keep = S::DENSE ? (pgok[q] && it * S::RT + row <= d_plim) : (row < left);
+            x[q][j] = keep ? v : NEG_INF;
             mx[S::RSPLIT ? q : 0] = fmaxf(mx[S::RSPLIT ? q : 0], x[q][j]);
           }
 #pragma unroll
@@ -912,7 +1024,9 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         for (int q = 0; q < 2; ++q)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float pj = fast_exp2(x[q][j] - m_run[S::RSPLIT ? q : 0]);
+            float pj = fast_exp2(x[q][j] - m_run[S::RSPLIT ? q : 0]);
+            // dense mode: a slot may see no valid position yet (reference unset)
+            if constexpr (S::DENSE) pj = (m_run[0] == NEG_INF) ? 0.f : pj;
             psum[S::RSPLIT ? q : 0] += pj;
             pb[4 * q + j] = (__bf16)pj;
           }
@@ -1161,7 +1275,9 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
   }
   __syncthreads();
   const bool split = a.write_partials != 0;
-  for (int item = tid; item < a.h * 64; item += S::NTHR) {
+  // (dense mode: `head` is the query slot m = row * h + head of the block)
+  const int n_items = (S::DENSE ? d_nr : 1) * a.h * 64;
+  for (int item = tid; item < n_items; item += S::NTHR) {
     const int head = item >> 6, c = item & 63;
     const int hgi = head >> 4, nn = head & 15;
     float M = NEG_INF;
@@ -1199,8 +1315,10 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
       for (int j = 0; j < 4; ++j)
         pk[j] = (uint32_t)f32_to_bf16_bits(acc[2 * j] * inv) |
                 ((uint32_t)f32_to_bf16_bits(acc[2 * j + 1] * inv) << 16);
-      *reinterpret_cast<u32x4*>(a.out + (int64_t)t * a.out_st + (int64_t)head * a.out_sh + 8 * c) = pk;
-      if (c == 0) a.lse[(int64_t)t * a.lse_st + head] = lse_v;
+      const int orow = S::DENSE ? d_r0 + head / a.h : t;
+      const int ohead = S::DENSE ? head - (head / a.h) * a.h : head;
+      *reinterpret_cast<u32x4*>(a.out + (int64_t)orow * a.out_st + (int64_t)ohead * a.out_sh + 8 * c) = pk;
+      if (c == 0) a.lse[(int64_t)orow * a.lse_st + ohead] = lse_v;
     } else {
       float* wo = a.ws_out + ((unit * a.h + head) * D_V) + 8 * c;
       f32x4 w0, w1;
@@ -1298,6 +1416,9 @@ using V_H4_C = Shape<4, 1, 32, 4, 0, true, true, false, true>;
 using N_H1_A = Shape<1, 4, 16, 2, 0, false, false, false, false, true>;
 using N_H2_A = Shape<2, 2, 32, 2, 0, false, false, false, false, true>;
 using N_H4_A = Shape<4, 1, 32, 4, 0, true, true, false, false, true>;
+// dense causal mode (576- and 512-wide rows)
+using D_H4 = Shape<4, 1, 32, 4, 0, true, true, false, false, false, true>;
+using D_H4_N = Shape<4, 1, 32, 4, 0, true, true, false, false, true, true>;
 using F_H1_A = Shape<2, 2, 32, 3, 1, false, false, true>;
 using F_H1_B = Shape<1, 2, 32, 3, 1>;
 using F_H2_A = Shape<2, 1, 32, 4, 1>;
@@ -1373,6 +1494,11 @@ hipError_t launch_fwd(const FwdArgs& a, int kv_format, int head_groups, int vari
     default: return hipErrorInvalidValue;
   }
 }
+hipError_t launch_dense(const FwdArgs& a, int nope, int64_t grid, hipStream_t stream) {
+  return nope ? launch_one<D_H4_N>(a, grid, stream) : launch_one<D_H4>(a, grid, stream);
+}
+int dense_lds_bytes(int nope) { return nope ? D_H4_N::LDS_BYTES : D_H4::LDS_BYTES; }
+
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)a.T, (unsigned)((a.h * 64 + 255) / 256));
   if (a.num_splits <= 4) hipLaunchKernelGGL(smla_lse_combine<4>, grid, dim3(256), 0, stream, a);

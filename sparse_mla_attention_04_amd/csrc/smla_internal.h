@@ -5,6 +5,10 @@
 
 namespace smla {
 
+// Index entries (or, in the dense mode, block-table pages) a work-group holds
+// in LDS per pass.
+constexpr int kListCap = 2048;
+
 // Everything a forward launch needs, passed by value as the kernel argument.
 struct FwdArgs {
   const uint16_t* q;          // bf16 [T, h, 576] (strided)
@@ -26,6 +30,10 @@ struct FwdArgs {
   int32_t write_partials;     // 1: write fp32 partials to ws_out / ws_lse instead of out / lse
   float scale_log2;           // softmax_scale * log2(e)
   int32_t bucket_shift;       // >= 0: gather each row's entries grouped by (slot >> shift), 16 groups; -1: list order
+  // dense causal mode only
+  const int32_t* query_start; // int32 [num_seqs + 1]: rows of sequence s are [query_start[s], query_start[s+1])
+  const int32_t* positions;   // int32 [T]: row t attends to positions 0 .. positions[t] of its sequence
+  int32_t dense_qb;           // query rows per work-group (64 / h)
 };
 
 struct CombineArgs {
@@ -49,5 +57,8 @@ bool fwd_shape(int kv_format, int head_groups, int variant, int nope, FwdShape* 
 hipError_t launch_fwd(const FwdArgs& a, int kv_format, int head_groups, int variant, int nope, int64_t grid,
                       hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+// Dense causal mode (bf16, rows of 576 or 512 dims): grid work-groups of 256 threads.
+hipError_t launch_dense(const FwdArgs& a, int nope, int64_t grid, hipStream_t stream);
+int dense_lds_bytes(int nope);
 
 }  // namespace smla

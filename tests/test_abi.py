@@ -95,6 +95,36 @@ def test_geometry_values():
         assert B.workspace_size(pn) == B.workspace_size(_params(num_heads=h))
 
 
+def _dense(p, q=16, kv=16, bt=16, qs=16, pos=16, out=16, lse=16):
+    L = B.lib()
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return L.sparse_mla_dense_fwd(ctypes.byref(p), v(q), v(kv), v(bt), v(qs), v(pos), v(out), v(lse), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kv_format="fp8"), B.SMLA_ERR_UNSUPPORTED),
+    (dict(index_mode="slot"), B.SMLA_ERR_UNSUPPORTED),
+    (dict(page_size=8), B.SMLA_ERR_UNSUPPORTED),
+    (dict(num_splits=2), B.SMLA_ERR_UNSUPPORTED),
+    (dict(tiling="pad64"), B.SMLA_ERR_UNSUPPORTED),
+    (dict(max_blocks_per_seq=4096), B.SMLA_ERR_UNSUPPORTED),
+    (dict(num_seqs=3000, max_blocks_per_seq=8), B.SMLA_ERR_UNSUPPORTED),
+    (dict(num_heads=0), B.SMLA_ERR_INVALID_ARG),
+    (dict(q_strides=(8 * 576, 570)), B.SMLA_ERR_INVALID_ARG),
+])
+def test_dense_bad_params_rejected(kw, code):
+    assert _dense(_params(**kw)) == code
+
+
+def test_dense_null_and_misaligned_pointers():
+    p = _params()
+    assert _dense(p, qs=None) == B.SMLA_ERR_INVALID_ARG
+    assert _dense(p, pos=None) == B.SMLA_ERR_INVALID_ARG
+    assert _dense(p, pos=18) == B.SMLA_ERR_INVALID_ARG
+    assert _dense(p, out=24) == B.SMLA_ERR_INVALID_ARG
+    assert _dense(_params(num_tokens=0), q=None, qs=None, pos=None) == B.SMLA_OK
+
+
 def test_bad_gather_order_rejected():
     for v in (-1, 3):
         p = _params()

@@ -594,3 +594,83 @@ def test_nope_recompute_and_two_chunks():
                      drop_frac=0.05, rope_dims=0)
     out, lse = to_np(*run_gpu(Dev(c), num_splits=1))
     check(out, lse, *oracle(c), what="nope topk 2100")
+
+
+# --------------------------------------------------------------------------- dense causal mode
+
+def _dense_inputs(c, positions=None):
+    """query_start / positions for a case whose rows are grouped by sequence,
+    and the index lists that express the same dense causal attention for the
+    oracle (row t lists 0 .. positions[t])."""
+    pos = c.positions if positions is None else positions
+    ns = c.block_table.shape[0]
+    counts = np.bincount(c.token_seq, minlength=ns)
+    qs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    width = int(pos.max()) + 1
+    idx = np.full((c.num_tokens, width), -1, dtype=np.int32)
+    for t in range(c.num_tokens):
+        idx[t, :pos[t] + 1] = np.arange(pos[t] + 1)
+    return qs, pos.astype(np.int32), idx
+
+
+def _run_dense(c, qs, pos, bt=None):
+    dev = Dev(c)
+    T, h = c.num_tokens, c.num_heads
+    out = torch.empty((T, h, 512), dtype=torch.bfloat16, device=dev.q.device)
+    lse = torch.empty((T, h), dtype=torch.float32, device=dev.q.device)
+    btd = dev.bt if bt is None else torch.from_numpy(bt).to(dev.q.device)
+    B.dense_fwd(dev.q, dev.kv, out, lse, block_table=btd, query_start=torch.from_numpy(qs).to(dev.q.device),
+                positions=torch.from_numpy(pos).to(dev.q.device), scale=c.scale, page_size=c.page_size)
+    return to_np(out, lse)
+
+
+@pytest.mark.parametrize("h,rope", [(8, 64), (12, 64), (16, 64), (64, 64), (8, 0), (32, 0)])
+def test_dense_matches_oracle(h, rope):
+    """Dense causal mode against the oracle with the full-prefix index lists,
+    over sequences of different lengths (one chunk starting at position 0)."""
+    say("dense", h, rope)
+    c = G.build_case("dense", seed=81, hist=[0, 100, 300, 1000], new=[20, 9, 17, 40], num_heads=h, topk=8,
+                     rope_dims=rope)
+    qs, pos, idx = _dense_inputs(c)
+    out, lse = _run_dense(c, qs, pos)
+    from oracle import sparse_mla_oracle as O
+    ro, rl = O.sparse_mla_forward(c.q, c.kv, idx, topk=idx.shape[1], scale=c.scale, index_mode="logical",
+                                  block_table=c.block_table, token_seq=c.token_seq)
+    check(out, lse, ro, rl, "dense h=%d rope=%d" % (h, rope))
+
+
+def test_dense_unsorted_positions_empty_sequence_and_bad_page():
+    """Positions in any order inside a sequence, a sequence with no query
+    rows, and a block-table page outside the pool (its positions are skipped,
+    as a sparse list entry on such a page is)."""
+    say("dense edge cases")
+    c = G.build_case("dense_edge", seed=82, hist=[200, 0, 500], new=[30, 0, 25], num_heads=8, topk=8)
+    rng = np.random.default_rng(5)
+    pos = c.positions.copy()
+    pos[:30] = rng.permutation(pos[:30])
+    bt = c.block_table.copy()
+    bt[2, 3] = c.num_pages + 7                     # positions 192..255 of sequence 2: skipped
+    qs, pos, idx = _dense_inputs(c, pos)
+    out, lse = _run_dense(c, qs, pos, bt=bt)
+    from oracle import sparse_mla_oracle as O
+    ro, rl = O.sparse_mla_forward(c.q, c.kv, idx, topk=idx.shape[1], scale=c.scale, index_mode="logical",
+                                  block_table=bt, token_seq=c.token_seq)
+    check(out, lse, ro, rl, "dense edges")
+
+
+def test_dense_8x2048_sampled_and_equal_to_sparse():
+    """Eight 2048-token prefill chunks (every row's prefix is within top-k):
+    sampled rows against the oracle, and every row against the sparse path
+    given the full-prefix index lists."""
+    say("dense 8x2048")
+    c = G.build_case("dense_8x2048", seed=83, hist=[0] * 8, new=[2048] * 8, num_heads=8, topk=2048)
+    qs, pos, idx = _dense_inputs(c)
+    out, lse = _run_dense(c, qs, pos)
+    rows = sorted(set([0, 2047, 2048, 16383] + list(np.random.default_rng(6).choice(16384, 24, replace=False))))
+    from oracle import sparse_mla_oracle as O
+    ro, rl = O.sparse_mla_forward(c.q, c.kv, idx, topk=2048, scale=c.scale, index_mode="logical",
+                                  block_table=c.block_table, token_seq=c.token_seq, rows=rows)
+    check(out[rows], lse[rows], ro, rl, "dense 8x2048 sampled")
+    dev = Dev(c, idx=idx)
+    so, sl = to_np(*run_gpu(dev, topk=2048, num_splits=1))
+    assert np.max(np.abs(so - out)) <= 1e-2 and np.max(np.abs(sl - lse)) <= SPLIT_ATOL
