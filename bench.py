@@ -20,6 +20,8 @@ Workloads (synthetic, seeded; `--workload`):
   c3_h{8,16,32,64}     4096 rows over 8 x (8192 + 512) tokens; suffix _pad64 for the padded tiling,
                        _nope for the NoPE geometry (512-wide rows, no rope part)
   c4_long_prefill      16384 rows, h=64, 65536-token history, locality-biased indices
+  dense_8x2048         the dense causal entry point on 8 prefill chunks of 2048 tokens
+                       from position 0, h=8 (every prefix within top-k)
 """
 from __future__ import annotations
 
@@ -73,6 +75,8 @@ def workload(name):
         return case, tiling, "c3_sweep" if rope else "c3_sweep_nope"
     if name in ("c1_tiny", "c2_decode", "c4_long_prefill", "c5_fp8") and rope:
         return G.make_config(name), tiling, name
+    if name == "dense_8x2048" and rope:
+        return G.build_case(name, seed=1006, hist=[0] * 8, new=[2048] * 8, num_heads=8, topk=2048), tiling, name
     raise SystemExit("unknown workload %s" % name)
 
 
@@ -166,12 +170,22 @@ def main():
     ws = B.workspace_for(p, "cuda")
     pws = torch.empty(max(16, pl.partials_bytes), dtype=torch.uint8, device="cuda")
 
+    dense = wl_name.startswith("dense")
+    if dense:
+        counts = np.bincount(case.token_seq, minlength=case.block_table.shape[0])
+        d_qs = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).cuda()
+        d_pos = torch.from_numpy(case.positions.astype(np.int32)).cuda()
+
     def step():
+        if dense:
+            B.dense_fwd(q, dev.kv, out, lse, block_table=dev.bt, query_start=d_qs, positions=d_pos,
+                        scale=case.scale, page_size=case.page_size)
+            return
         B.fwd(q, dev.kv, dev.idx, out, lse, topk=case.topk, scale=case.scale, workspace=ws,
               block_table=dev.bt, token_seq=dev.ts, params=p)
 
     def kernel_only():
-        if pl.num_splits > 1:
+        if pl.num_splits > 1 and not dense:
             B.fwd_partials(q, dev.kv, dev.idx, pws, topk=case.topk, scale=case.scale, block_table=dev.bt,
                            token_seq=dev.ts, params=p)
         else:
@@ -260,13 +274,14 @@ def main():
     cold_ms = float(np.median(cold))
     del flush
 
-    n_valid = algorithmic_counts(case)
+    # dense: every row attends to its whole prefix (positions + 1 cache rows)
+    n_valid = int((case.positions.astype(np.int64) + 1).sum()) if dense else algorithmic_counts(case)
     d_qk = int(case.q.shape[2])
     row_bytes = 2 * d_qk if case.kv_format == "bf16" else 656
     gathered = n_valid * row_bytes
     flops = n_valid * h * 2 * (d_qk + 512)
     tokens_per_s = T / (ms_per_step * 1e-3)
-    hbm_bound = h < 64
+    hbm_bound = h < 64 and not dense
     if hbm_bound:
         achieved = gathered / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -278,7 +293,7 @@ def main():
     traffic, traffic_note = counted_traffic(args.workload)
     roof["traffic"] = None if traffic is None else round(traffic)
     roof["traffic_note"] = traffic_note
-    roof["kernel"] = "smla_fwd" + ("" if pl.num_splits == 1 else " (split partials)")
+    roof["kernel"] = "smla_fwd" + (" (dense causal)" if dense else "" if pl.num_splits == 1 else " (split partials)")
     roof["kernel_us"] = round(kern_ms * 1e3, 2)
     roof["kernel_us_p10_p50_p90"] = [round(float(np.percentile(kern_all, q)) * 1e3, 2) for q in (10, 50, 90)]
     roof["algorithmic_bytes"] = gathered
@@ -297,7 +312,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl_name, "num_tokens": T, "num_heads": h, "topk": case.topk,
+        "config": {"workload": wl_name, "entry": "sparse_mla_dense_fwd" if dense else "sparse_mla_fwd",
+                   "num_tokens": T, "num_heads": h, "topk": case.topk,
                    "kv_format": case.kv_format, "page_size": case.page_size, "tiling": tiling,
                    "num_splits": pl.num_splits, "kernel_variant": args.variant,
                    "gather_order": {1: "list", 2: "slot"}[pl.gather_order],
