@@ -22,6 +22,8 @@ Workloads (synthetic, seeded; `--workload`):
   c4_long_prefill      16384 rows, h=64, 65536-token history, locality-biased indices
   dense_8x2048         the dense causal entry point on 8 prefill chunks of 2048 tokens
                        from position 0, h=8 (every prefix within top-k)
+  topk_4096x65536      the per-row top-k selection: 4096 rows of 65536 fp32 scores
+                       (N(0,1) from a seeded device generator), k = 2048
 """
 from __future__ import annotations
 
@@ -139,6 +141,41 @@ def cpu_baseline(case, seconds):
                       "numpy fp64 oracle" % (done, T, el)}
 
 
+def bench_topk(args):
+    """The indexer's top-k step alone: rows/s, against HBM (one read of the
+    scores plus the index write per launch)."""
+    import torch
+    from sparse_mla_attention_04_amd import binding as B
+    T, N, k = 4096, 65536, 2048
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1007)
+    scores = torch.randn((T, N), generator=g, device="cuda", dtype=torch.float32)
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    step = lambda: B.topk(scores, k, out=idx)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    algo = T * N * 4 + T * k * 4
+    achieved = algo / (ms * 1e-3) / 1e9
+    res = {"metric": "sparse MLA indexer top-k: query rows/s", "value": round(T / (ms * 1e-3), 1),
+           "unit": "query-rows/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f32", "data": "synthetic (seeded device N(0,1))",
+           "config": {"workload": "topk_4096x65536", "num_rows": T, "num_keys": N, "k": k},
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                        "kernel": "smla_topk_kernel", "kernel_us": round(ms * 1e3, 2),
+                        "algorithmic_bytes": algo}}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -157,6 +194,8 @@ def main():
     from sparse_mla_attention_04_amd import binding as B
     from sparse_mla_attention_04_amd.inputs import DeviceCase as Dev
 
+    if args.workload == "topk_4096x65536":
+        return bench_topk(args)
     case, tiling, wl_name = workload(args.workload)
     dev = Dev(case)
     T, h = case.num_tokens, case.num_heads

@@ -258,6 +258,26 @@ int sparse_mla_dense_fwd(const smla_params* p, const void* q, const void* kv_cac
                          const int32_t* block_table, const int32_t* query_start,
                          const int32_t* positions, void* out, float* lse, void* stream);
 
+/* Per-row top-k selection: the last step of the sparse indexer, producing
+ * the int32 index lists the attention consumes (vLLM PR #54951, "Summary":
+ * each query row keeps the indices of its top-k scored keys; "Additional
+ * checks": selected sets are compared, the order inside a row is not
+ * defined).  The score function itself is not on the pages and is not part
+ * of this library: the caller passes the scores.
+ *   scores  fp32 [num_rows, ld] (device, ld >= n_keys elements, 4-B aligned)
+ *   lens    int32 [num_rows] (device) or NULL: row t's valid keys are
+ *           0 .. lens[t]-1, clamped to [0, n_keys] (NULL: all n_keys)
+ *   idx     int32 [num_rows, idx_stride] (device, idx_stride >= k): receives
+ *           min(k, lens[t]) selected key indices in an unspecified order,
+ *           then -1 in the remaining columns of the first k
+ * Selection order: higher score first, NaN below every number (-inf
+ * included), equal scores by lower key index.  Errors: SMLA_ERR_INVALID_ARG
+ * for negative sizes, k < 1, ld < n_keys, idx_stride < k, null or
+ * misaligned pointers (nothing is launched); SMLA_ERR_HIP on launch failure.
+ * Enqueued on `stream`; no allocation, no synchronisation. */
+int sparse_mla_topk(const float* scores, int64_t ld, const int32_t* lens, int32_t num_rows,
+                    int32_t n_keys, int32_t k, int32_t* idx, int64_t idx_stride, void* stream);
+
 /* Static, human-readable text for a status code. */
 const char* sparse_mla_status_string(int status);
 

@@ -31,7 +31,7 @@ D_QK, D_V = 576, 512
 
 EXPORTS = ("sparse_mla_workspace_size", "sparse_mla_plan", "sparse_mla_plan_for",
            "sparse_mla_fwd", "sparse_mla_fwd_partials", "sparse_mla_lse_combine",
-           "sparse_mla_status_string", "sparse_mla_dense_fwd")
+           "sparse_mla_status_string", "sparse_mla_dense_fwd", "sparse_mla_topk")
 
 
 class Params(ctypes.Structure):
@@ -101,6 +101,10 @@ def lib() -> ctypes.CDLL:
         L.sparse_mla_lse_combine.restype = ctypes.c_int
         L.sparse_mla_dense_fwd.argtypes = [ctypes.POINTER(Params)] + [ctypes.c_void_p] * 8
         L.sparse_mla_dense_fwd.restype = ctypes.c_int
+        L.sparse_mla_topk.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
+                                      ctypes.c_void_p]
+        L.sparse_mla_topk.restype = ctypes.c_int
         L.sparse_mla_status_string.argtypes = [ctypes.c_int]
         L.sparse_mla_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -225,6 +229,23 @@ def dense_fwd(q, kv, out, lse, *, block_table, query_start, positions, scale: fl
                                     _ptr(positions), _ptr(out), _ptr(lse), ctypes.c_void_p(int(stream)))
     if rc != SMLA_OK:
         raise SparseMLAError(rc, "sparse_mla_dense_fwd")
+
+
+def topk(scores, k: int, *, lens=None, out=None, stream=None):
+    """sparse_mla_topk on torch tensors: scores fp32 [T, N] (rows contiguous),
+    lens int32 [T] or None; returns (or fills) int32 [T, k] index rows."""
+    import torch
+    T, N = int(scores.shape[0]), int(scores.shape[1])
+    assert scores.dtype == torch.float32 and scores.stride(1) == 1
+    if out is None:
+        out = torch.empty((T, k), dtype=torch.int32, device=scores.device)
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    rc = lib().sparse_mla_topk(_ptr(scores), int(scores.stride(0)), _ptr(lens), T, N, k, _ptr(out),
+                               int(out.stride(0)), ctypes.c_void_p(int(stream)))
+    if rc != SMLA_OK:
+        raise SparseMLAError(rc, "sparse_mla_topk")
+    return out
 
 
 def fwd_partials(q, kv, topk_idx, workspace, *, topk: int, scale: float, page_size: int = 64,

@@ -369,6 +369,25 @@ int sparse_mla_dense_fwd(const smla_params* p, const void* q, const void* kv_cac
   return SMLA_OK;
 }
 
+int sparse_mla_topk(const float* scores, int64_t ld, const int32_t* lens, int32_t num_rows, int32_t n_keys,
+                    int32_t k, int32_t* idx, int64_t idx_stride, void* stream) {
+  if (num_rows < 0 || n_keys < 0 || k < 1 || ld < n_keys || idx_stride < k) return SMLA_ERR_INVALID_ARG;
+  if (num_rows == 0) return SMLA_OK;
+  if (!scores || !idx || !aligned(scores, 4) || !aligned(idx, 4) || (lens && !aligned(lens, 4)))
+    return SMLA_ERR_INVALID_ARG;
+  smla::TopkArgs a{};
+  a.scores = scores;
+  a.lens = lens;
+  a.idx = idx;
+  a.ld = ld;
+  a.idx_stride = idx_stride;
+  a.T = num_rows;
+  a.n_keys = n_keys;
+  a.k = k;
+  if (smla::launch_topk(a, static_cast<hipStream_t>(stream)) != hipSuccess) return SMLA_ERR_HIP;
+  return SMLA_OK;
+}
+
 const char* sparse_mla_status_string(int status) {
   switch (status) {
     case SMLA_OK: return "ok";

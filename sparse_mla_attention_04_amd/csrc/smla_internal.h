@@ -45,6 +45,16 @@ struct CombineArgs {
   int32_t T, h, num_splits;
 };
 
+// Per-row top-k selection.
+struct TopkArgs {
+  const float* scores;        // fp32 [T, ld]
+  const int32_t* lens;        // int32 [T] valid keys per row, or null (n_keys)
+  int32_t* idx;               // int32 [T, idx_stride]
+  int64_t ld, idx_stride;
+  int32_t T, n_keys, k;
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
+
 // Pipeline shape of one forward kernel instantiation.
 struct FwdShape {
   int head_groups, row_groups, tile_rows, stages, threads, lds_bytes;

@@ -215,3 +215,20 @@ def test_status_strings():
     for s in range(5):
         assert B.status_string(s)
     assert "unknown" in B.status_string(99)
+
+
+def _topk(scores=16, ld=100, lens=None, rows=4, n=100, k=8, idx=16, idx_stride=8):
+    L = B.lib()
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return L.sparse_mla_topk(v(scores), ld, v(lens), rows, n, k, v(idx), idx_stride, None)
+
+
+@pytest.mark.parametrize("kw", [dict(rows=-1), dict(n=-1), dict(k=0), dict(ld=99), dict(idx_stride=7),
+                                dict(scores=None), dict(idx=None), dict(scores=18), dict(idx=2),
+                                dict(lens=6)])
+def test_topk_bad_args_rejected(kw):
+    assert _topk(**kw) == B.SMLA_ERR_INVALID_ARG
+
+
+def test_topk_empty_batch_is_ok():
+    assert _topk(rows=0, scores=None, idx=None) == B.SMLA_OK
