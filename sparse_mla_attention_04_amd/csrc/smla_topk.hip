@@ -5,9 +5,9 @@
 // order inside a row is not defined).
 //
 // One work-group (four waves) per query row.  The k-th largest score is found
-// by a radix select over an order-preserving 32-bit key, eight bits per round
-// with a 256-bin LDS histogram; a final pass writes every key above it (in any
-// order) and the lowest-index keys equal to it (in index order).
+// by a radix select over an order-preserving 32-bit key (three rounds of an
+// LDS histogram); a final pass writes every key above it (in any order) and
+// the lowest-index keys equal to it (in index order).
 #include "smla_internal.h"
 
 namespace smla {
@@ -23,12 +23,21 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// Digits of the radix select, most significant first: 11 + 11 + 10 bits, so
+// the first histogram already spreads typical scores (sign, exponent and two
+// mantissa bits) over many bins.
+constexpr int NB = 2048;                 // bins of the widest digit
+constexpr int SHIFTS[3] = {21, 10, 0};
+constexpr int WIDTHS[3] = {11, 11, 10};
+
 __global__ void __launch_bounds__(256) smla_topk_kernel(TopkArgs a) {
-  __shared__ uint32_t hist[256];
-  __shared__ int ctl[4];    // chosen digit, keys still to take in its bucket, above-count, tie-count
+  __shared__ uint32_t hist[NB];
+  __shared__ int part[256];  // per-thread bin sums (suffix-scanned)
+  __shared__ int ctl[4];     // chosen digit, keys still to take in its bucket, above-count, tie-count
   __shared__ int wsum[4];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const float* row = a.scores + (int64_t)t * a.ld;
   int32_t* out = a.idx + (int64_t)t * a.idx_stride;
   int len = a.lens ? a.lens[t] : a.n_keys;
@@ -42,17 +51,39 @@ __global__ void __launch_bounds__(256) smla_topk_kernel(TopkArgs a) {
   // the keys above that bucket (k - kr of them) are all selected
   uint32_t prefix = 0, mask = 0;
   int kr = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[tid] = 0u;
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = SHIFTS[pass];
+    const int nb = 1 << WIDTHS[pass];
+    for (int i = tid; i < nb; i += 256) hist[i] = 0u;
     __syncthreads();
     for (int i = tid; i < len; i += 256) {
       const uint32_t u = order_key(row[i]);
-      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & (uint32_t)(nb - 1)], 1u);
     }
     __syncthreads();
-    if (tid == 0) {
-      int acc = 0, d = 255;
-      for (; d > 0; --d) {
+    // thread j owns bins [j * per, (j + 1) * per); suffix sums over threads
+    // (from the top bin down) locate the bin where the count reaches kr
+    const int per = nb / 256;
+    int own = 0;
+    for (int q = 0; q < per; ++q) own += (int)hist[tid * per + q];
+    // inclusive suffix sum over thread index, high to low: scan the reversed order
+    int incl = own;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_down(incl, d, 64);
+      if (lane + d < 64) incl += v;
+    }
+    if (lane == 0) wsum[wave] = incl;   // the wave's total
+    __syncthreads();
+    int above_waves = 0;
+    for (int w = wave + 1; w < 4; ++w) above_waves += wsum[w];
+    const int suffix = incl + above_waves;          // keys in bins owned by threads >= tid
+    const int above_me = suffix - own;              // keys in bins owned by threads > tid
+    if (above_me < kr && suffix >= kr) {
+      // the crossing bin is one of this thread's
+      int acc = above_me, d = (tid + 1) * per - 1;
+      for (; d > tid * per; --d) {
         if (acc + (int)hist[d] >= kr) break;
         acc += (int)hist[d];
       }
@@ -61,7 +92,7 @@ __global__ void __launch_bounds__(256) smla_topk_kernel(TopkArgs a) {
     }
     __syncthreads();
     prefix |= (uint32_t)ctl[0] << shift;
-    mask |= 255u << shift;
+    mask |= (uint32_t)(nb - 1) << shift;
     kr = ctl[1];
     __syncthreads();
   }
@@ -72,7 +103,6 @@ __global__ void __launch_bounds__(256) smla_topk_kernel(TopkArgs a) {
     ctl[3] = 0;
   }
   __syncthreads();
-  const int lane = tid & 63, wave = tid >> 6;
   for (int base = 0; base < len; base += 256) {
     const int i = base + tid;
     const uint32_t u = i < len ? order_key(row[i]) : 0u;
