@@ -13,6 +13,8 @@
 namespace smla {
 namespace {
 
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
 // Order-preserving key of a score: larger score -> larger key, equal scores
 // (-0 and +0 included) -> equal keys; NaN maps below every number (-inf
 // included).
@@ -47,6 +49,7 @@ __global__ void __launch_bounds__(256) smla_topk_kernel(TopkArgs a) {
     for (int i = tid; i < k; i += 256) out[i] = i < len ? i : -1;
     return;
   }
+  const bool vec = ((reinterpret_cast<uintptr_t>(row) & 15u) == 0) && ((a.ld & 3) == 0);
   // invariant: at least kr of the keys matching (prefix, mask) remain, and
   // the keys above that bucket (k - kr of them) are all selected
   uint32_t prefix = 0, mask = 0;
@@ -57,10 +60,27 @@ __global__ void __launch_bounds__(256) smla_topk_kernel(TopkArgs a) {
     const int nb = 1 << WIDTHS[pass];
     for (int i = tid; i < nb; i += 256) hist[i] = 0u;
     __syncthreads();
-    for (int i = tid; i < len; i += 256) {
-      const uint32_t u = order_key(row[i]);
+    auto count = [&](float x) {
+      const uint32_t u = order_key(x);
       if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & (uint32_t)(nb - 1)], 1u);
+    };
+    // 16-byte loads (four scores per lane, four loads in flight) when the
+    // row allows them; the last len % 4 scores one by one
+    int done = 0;
+    if (vec) {
+      const f32x4* row4 = reinterpret_cast<const f32x4*>(row);
+      const int n4 = len >> 2;
+#pragma unroll 4
+      for (int j = tid; j < n4; j += 256) {
+        const f32x4 v = row4[j];
+        count(v[0]);
+        count(v[1]);
+        count(v[2]);
+        count(v[3]);
+      }
+      done = n4 << 2;
     }
+    for (int i = done + tid; i < len; i += 256) count(row[i]);
     __syncthreads();
     // thread j owns bins [j * per, (j + 1) * per); suffix sums over threads
     // (from the top bin down) locate the bin where the count reaches kr
@@ -103,7 +123,49 @@ __global__ void __launch_bounds__(256) smla_topk_kernel(TopkArgs a) {
     ctl[3] = 0;
   }
   __syncthreads();
-  for (int base = 0; base < len; base += 256) {
+  int tail0 = 0;
+  if (vec) {
+    // chunks of 1024 scores, four consecutive ones per thread (thread order
+    // is index order); ties ranked by a wave scan of the per-thread counts
+    const f32x4* row4 = reinterpret_cast<const f32x4*>(row);
+    const int n4 = len >> 2;
+    for (int b4 = 0; b4 < n4; b4 += 256) {
+      const int j = b4 + tid;
+      const bool ok = j < n4;
+      f32x4 v = ok ? row4[j] : f32x4{0.f, 0.f, 0.f, 0.f};
+      bool tq[4];
+      int ties = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t u = order_key(v[q]);
+        if (ok && u > prefix) out[atomicAdd(&ctl[2], 1)] = 4 * j + q;
+        tq[q] = ok && u == prefix;
+        ties += tq[q] ? 1 : 0;
+      }
+      int incl = ties;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int t2 = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += t2;
+      }
+      if (lane == 63) wsum[wave] = incl;
+      __syncthreads();
+      int r = ctl[3] + incl - ties;
+      for (int w = 0; w < wave; ++w) r += wsum[w];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (tq[q]) {
+          if (r < kr) out[(k - kr) + r] = 4 * j + q;
+          ++r;
+        }
+      }
+      __syncthreads();
+      if (tid == 0) ctl[3] += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+      __syncthreads();
+    }
+    tail0 = n4 << 2;
+  }
+  for (int base = tail0; base < len; base += 256) {
     const int i = base + tid;
     const uint32_t u = i < len ? order_key(row[i]) : 0u;
     const bool above = i < len && u > prefix;

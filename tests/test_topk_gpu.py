@@ -25,7 +25,8 @@ def _check(scores, lens, k):
     assert bad.size == 0, "rows %s differ" % bad[:8]
 
 
-@pytest.mark.parametrize("seed,T,N,k", [(1, 40, 5000, 2048), (2, 17, 3000, 1), (3, 9, 300, 256)])
+@pytest.mark.parametrize("seed,T,N,k", [(1, 40, 5000, 2048), (2, 17, 3000, 1), (3, 9, 300, 256),
+                                         (4, 11, 4001, 100)])      # odd row stride: 4-byte loads
 def test_topk_random_rows(seed, T, N, k):
     say("topk random", seed, T, N, k)
     rng = np.random.default_rng(seed)
