@@ -1038,28 +1038,27 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         const LDS_AS uint8_t* tp = tptr(itq);
         if constexpr (S::RSPLIT) {
           // k-step kk's K operand (this wave's 16 rows) feeds the MFMAs of both
-          // head groups; chain (group, kk mod 2) is fed every 4th MFMA
+          // head groups, one accumulation chain per group
           constexpr int KR = 4;
           bf16x8 kr[S::KS];
 #pragma unroll
           for (int i = 0; i < KR; ++i)
             kr[i] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + krs[i & 1] + (i >> 1) * S::RT * 128);
           __builtin_amdgcn_sched_group_barrier(0x100, KR, 0);
-          f32x4 acc[2][2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) acc[e][0] = acc[e][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+          f32x4 acc[2];
+          acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kk = 0; kk < S::KS; ++kk) {
 #pragma unroll
             for (int e = 0; e < 2; ++e)
-              acc[e][kk & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[kk], qb[18 * e + kk], acc[e][kk & 1], 0, 0, 0);
+              acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[kk], qb[18 * e + kk], acc[e], 0, 0, 0);
             const int j = kk + KR;
             if (j < S::KS) kr[j] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + krs[j & 1] + (j >> 1) * S::RT * 128);
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             if (j < S::KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
-#pragma unroll
-          for (int e = 0; e < 2; ++e) out[e] = acc[e][0] + acc[e][1];
+          out[0] = acc[0];
+          out[1] = acc[1];
           return;
         }
         // MFMA i is (fragment i & 1, k-step i >> 1), accumulating into its
