@@ -5,9 +5,14 @@
 // order inside a row is not defined).
 //
 // One work-group (four waves) per query row.  The k-th largest score is found
-// by a radix select over an order-preserving 32-bit key (three rounds of an
-// LDS histogram); a final pass writes every key above it (in any order) and
-// the lowest-index keys equal to it (in index order).
+// by a radix select over an order-preserving 32-bit key: an LDS histogram of
+// the key's top 11 bits over the whole row names the bucket holding the k-th
+// key.  When that bucket fits in LDS, a second read of the row writes every
+// key above the bucket and copies the bucket's keys to LDS, where the
+// remaining 11 + 10 bits are resolved and ties are cut by index (two reads of
+// the row in all).  A larger bucket (heavily tied rows) takes two more
+// histogram rounds over the row and a final pass that writes the keys above
+// the k-th key and the lowest-index keys equal to it.
 #include "smla_internal.h"
 
 namespace smla {
@@ -31,12 +36,53 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 constexpr int NB = 2048;                 // bins of the widest digit
 constexpr int SHIFTS[3] = {21, 10, 0};
 constexpr int WIDTHS[3] = {11, 11, 10};
+// keys of the top-digit bucket held in LDS (N(0,1) scores, 65536 keys,
+// k = 2048: about 1200)
+constexpr int CAP = 3072;
+
+// Radix step on a filled histogram of nb bins: the bin in which the count of
+// keys, taken from the top bin down, reaches kr.  Thread j owns bins
+// [j * per, (j + 1) * per); suffix sums over the threads locate the owner of
+// the crossing bin, which writes ctl[0] = bin, ctl[1] = keys still to take
+// inside it, ctl[4] = the bin's count.  Ends with a barrier.
+__device__ __forceinline__ void find_bin(const uint32_t* hist, int nb, int kr, int* ctl, int* wsum, int tid,
+                                         int lane, int wave) {
+  const int per = nb / 256;
+  int own = 0;
+  for (int q = 0; q < per; ++q) own += (int)hist[tid * per + q];
+  // inclusive suffix sum over thread index, high to low
+  int incl = own;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_down(incl, d, 64);
+    if (lane + d < 64) incl += v;
+  }
+  if (lane == 0) wsum[wave] = incl;   // the wave's total
+  __syncthreads();
+  int above_waves = 0;
+  for (int w = wave + 1; w < 4; ++w) above_waves += wsum[w];
+  const int suffix = incl + above_waves;          // keys in bins owned by threads >= tid
+  const int above_me = suffix - own;              // keys in bins owned by threads > tid
+  if (above_me < kr && suffix >= kr) {
+    int acc = above_me, d = (tid + 1) * per - 1;
+    for (; d > tid * per; --d) {
+      if (acc + (int)hist[d] >= kr) break;
+      acc += (int)hist[d];
+    }
+    ctl[0] = d;
+    ctl[1] = kr - acc;
+    ctl[4] = (int)hist[d];
+  }
+  __syncthreads();
+}
 
 __global__ void __launch_bounds__(256) smla_topk_kernel(TopkArgs a) {
   __shared__ uint32_t hist[NB];
   __shared__ int part[256];  // per-thread bin sums (suffix-scanned)
-  __shared__ int ctl[4];     // chosen digit, keys still to take in its bucket, above-count, tie-count
+  __shared__ int ctl[8];     // chosen digit, keys still to take in its bucket, above-count, tie-count, bin count
   __shared__ int wsum[4];
+  __shared__ uint32_t cand_key[CAP];   // the top-digit bucket's keys and indices
+  __shared__ int32_t cand_idx[CAP];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -54,10 +100,7 @@ __global__ void __launch_bounds__(256) smla_topk_kernel(TopkArgs a) {
   // the keys above that bucket (k - kr of them) are all selected
   uint32_t prefix = 0, mask = 0;
   int kr = k;
-#pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = SHIFTS[pass];
-    const int nb = 1 << WIDTHS[pass];
+  auto hist_pass = [&](int shift, int nb) {
     for (int i = tid; i < nb; i += 256) hist[i] = 0u;
     __syncthreads();
     auto count = [&](float x) {
@@ -82,40 +125,112 @@ __global__ void __launch_bounds__(256) smla_topk_kernel(TopkArgs a) {
     }
     for (int i = done + tid; i < len; i += 256) count(row[i]);
     __syncthreads();
-    // thread j owns bins [j * per, (j + 1) * per); suffix sums over threads
-    // (from the top bin down) locate the bin where the count reaches kr
-    const int per = nb / 256;
-    int own = 0;
-    for (int q = 0; q < per; ++q) own += (int)hist[tid * per + q];
-    // inclusive suffix sum over thread index, high to low: scan the reversed order
-    int incl = own;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int v = __shfl_down(incl, d, 64);
-      if (lane + d < 64) incl += v;
-    }
-    if (lane == 0) wsum[wave] = incl;   // the wave's total
-    __syncthreads();
-    int above_waves = 0;
-    for (int w = wave + 1; w < 4; ++w) above_waves += wsum[w];
-    const int suffix = incl + above_waves;          // keys in bins owned by threads >= tid
-    const int above_me = suffix - own;              // keys in bins owned by threads > tid
-    if (above_me < kr && suffix >= kr) {
-      // the crossing bin is one of this thread's
-      int acc = above_me, d = (tid + 1) * per - 1;
-      for (; d > tid * per; --d) {
-        if (acc + (int)hist[d] >= kr) break;
-        acc += (int)hist[d];
-      }
-      ctl[0] = d;
-      ctl[1] = kr - acc;
-    }
-    __syncthreads();
+    find_bin(hist, nb, kr, ctl, wsum, tid, lane, wave);
     prefix |= (uint32_t)ctl[0] << shift;
     mask |= (uint32_t)(nb - 1) << shift;
     kr = ctl[1];
+  };
+  // invariant: at least kr of the keys matching (prefix, mask) remain, and
+  // the keys above that bucket (k - kr of them) are all selected
+  hist_pass(SHIFTS[0], 1 << WIDTHS[0]);
+  const int nbucket = ctl[4];
+  if (nbucket <= CAP) {
+    // ---- second read: keys above the bucket out, the bucket's keys to LDS
+    const uint32_t d0 = prefix >> SHIFTS[0];
     __syncthreads();
+    if (tid == 0) {
+      ctl[2] = 0;
+      ctl[3] = 0;
+    }
+    __syncthreads();
+    auto route = [&](float x, int i) {
+      const uint32_t u = order_key(x);
+      const uint32_t d = u >> SHIFTS[0];
+      if (d > d0) {
+        out[atomicAdd(&ctl[2], 1)] = i;
+      } else if (d == d0) {
+        const int c = atomicAdd(&ctl[3], 1);
+        cand_key[c] = u;
+        cand_idx[c] = i;
+      }
+    };
+    int done = 0;
+    if (vec) {
+      const f32x4* row4 = reinterpret_cast<const f32x4*>(row);
+      const int n4 = len >> 2;
+#pragma unroll 4
+      for (int j = tid; j < n4; j += 256) {
+        const f32x4 v = row4[j];
+        route(v[0], 4 * j);
+        route(v[1], 4 * j + 1);
+        route(v[2], 4 * j + 2);
+        route(v[3], 4 * j + 3);
+      }
+      done = n4 << 2;
+    }
+    for (int i = done + tid; i < len; i += 256) route(row[i], i);
+    __syncthreads();
+    const int nc = ctl[3];   // == nbucket
+    // ---- the remaining digits over the LDS copy of the bucket
+#pragma unroll
+    for (int pass = 1; pass < 3; ++pass) {
+      const int shift = SHIFTS[pass];
+      const int nb = 1 << WIDTHS[pass];
+      for (int i = tid; i < nb; i += 256) hist[i] = 0u;
+      __syncthreads();
+      for (int c = tid; c < nc; c += 256) {
+        const uint32_t u = cand_key[c];
+        if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & (uint32_t)(nb - 1)], 1u);
+      }
+      __syncthreads();
+      find_bin(hist, nb, kr, ctl, wsum, tid, lane, wave);
+      prefix |= (uint32_t)ctl[0] << shift;
+      mask |= (uint32_t)(nb - 1) << shift;
+      kr = ctl[1];
+    }
+    // prefix is the k-th largest key; kr of the n_eq keys equal to it are
+    // taken, the kr lowest-index ones
+    const int n_eq = ctl[4];
+    uint32_t vsel = 0u;   // ties are taken while ~index >= vsel
+    if (n_eq > kr) {
+      // radix select of the kr-th largest ~index among the ties (indices are
+      // distinct, so exactly kr ties reach it)
+      uint32_t vpre = 0u, vmask = 0u;
+      int kv = kr;
+#pragma unroll
+      for (int pass = 0; pass < 3; ++pass) {
+        const int shift = SHIFTS[pass];
+        const int nb = 1 << WIDTHS[pass];
+        __syncthreads();
+        for (int i = tid; i < nb; i += 256) hist[i] = 0u;
+        __syncthreads();
+        for (int c = tid; c < nc; c += 256) {
+          const uint32_t v = ~(uint32_t)cand_idx[c];
+          if (cand_key[c] == prefix && (v & vmask) == vpre) atomicAdd(&hist[(v >> shift) & (uint32_t)(nb - 1)], 1u);
+        }
+        __syncthreads();
+        find_bin(hist, nb, kv, ctl, wsum, tid, lane, wave);
+        vpre |= (uint32_t)ctl[0] << shift;
+        vmask |= (uint32_t)(nb - 1) << shift;
+        kv = ctl[1];
+      }
+      vsel = vpre;
+    }
+    __syncthreads();
+    if (tid == 0) ctl[3] = 0;
+    __syncthreads();
+    for (int c = tid; c < nc; c += 256) {
+      const uint32_t u = cand_key[c];
+      if (u > prefix) {
+        out[atomicAdd(&ctl[2], 1)] = cand_idx[c];
+      } else if (u == prefix && ~(uint32_t)cand_idx[c] >= vsel) {
+        out[(k - kr) + atomicAdd(&ctl[3], 1)] = cand_idx[c];
+      }
+    }
+    return;
   }
+  hist_pass(SHIFTS[1], 1 << WIDTHS[1]);
+  hist_pass(SHIFTS[2], 1 << WIDTHS[2]);
   // prefix is the k-th largest key: the k - kr keys above it go to
   // out[0 .. k - kr), the kr lowest-index keys equal to it to out[k - kr .. k)
   if (tid == 0) {

@@ -186,6 +186,10 @@ def test_plan_for_is_pure_and_splits_small_batches():
     assert pl.num_splits == 5 and pl.units == 250 and pl.grid == 256
     pl = B.plan(_params(num_tokens=20, topk=256, num_heads=64), num_cus=256)
     assert pl.num_splits == 8 and pl.units == 160 and pl.grid == 160
+    # one head group: every split keeps at least 256 list entries
+    assert B.plan(_params(num_tokens=64, topk=128, num_heads=8), num_cus=256).num_splits == 1
+    assert B.plan(_params(num_tokens=64, topk=512, num_heads=8), num_cus=256).num_splits == 2
+    assert B.plan(_params(num_tokens=64, topk=128, num_heads=32), num_cus=256).num_splits == 2
     # head tiles
     assert B.plan(_params(num_heads=32), num_cus=256).head_groups == 2
     assert B.plan(_params(num_heads=64), num_cus=256).head_groups == 4

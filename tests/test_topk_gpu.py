@@ -59,3 +59,21 @@ def test_topk_long_rows():
     rng = np.random.default_rng(5)
     s = rng.standard_normal((48, 65536)).astype(np.float32)
     _check(s, rng.integers(60000, 65537, size=48), 2048)
+
+
+def test_topk_tied_threshold_bucket():
+    """The threshold score shared by more keys than are taken, the bucket small
+    enough to be resolved in LDS (ties cut by index there), next to rows whose
+    threshold bucket is larger than that (resolved over the row)."""
+    say("topk tied threshold bucket")
+    rng = np.random.default_rng(6)
+    T, N = 12, 9000
+    s = (-np.abs(rng.standard_normal((T, N))) - 3.0).astype(np.float32)
+    for t in range(T):
+        n_tie = [2500, 2100, 3000, 2049, 6000, 9000][t % 6]
+        n_hi = [0, 500, 1000, 0, 100, 0][t % 6]
+        pos = rng.permutation(N)
+        s[t, pos[:n_tie]] = 1.0
+        s[t, pos[n_tie:n_tie + n_hi]] = 2.0 + rng.random(n_hi).astype(np.float32)
+    _check(s, None, 2048)
+    _check(s, rng.integers(2049, N + 1, size=T), 2048)
