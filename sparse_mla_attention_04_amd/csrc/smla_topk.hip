@@ -36,9 +36,13 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 constexpr int NB = 2048;                 // bins of the widest digit
 constexpr int SHIFTS[3] = {21, 10, 0};
 constexpr int WIDTHS[3] = {11, 11, 10};
-// keys of the top-digit bucket held in LDS (N(0,1) scores, 65536 keys,
-// k = 2048: about 1200)
-constexpr int CAP = 3072;
+// Keys of the top-digit bucket held in LDS (N(0,1) scores, 65536 keys,
+// k = 2048: about 1200).  24 KB of LDS per work-group lets six run on a CU;
+// measured on MI355X (4096 x 65536, k = 2048): 0.52 ms with room for 3072
+// keys, 0.47 ms for 2048 or 1536, 0.82 ms for 1024 (the bucket no longer
+// fits and rows take the four-read path); histogram copies against LDS
+// atomic collisions and deeper load unrolling did not help.
+constexpr int CAP = 2048;
 
 // Radix step on a filled histogram of nb bins: the bin in which the count of
 // keys, taken from the top bin down, reaches kr.  Thread j owns bins
@@ -78,7 +82,6 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, int nb, int kr, i
 
 __global__ void __launch_bounds__(256) smla_topk_kernel(TopkArgs a) {
   __shared__ uint32_t hist[NB];
-  __shared__ int part[256];  // per-thread bin sums (suffix-scanned)
   __shared__ int ctl[8];     // chosen digit, keys still to take in its bucket, above-count, tie-count, bin count
   __shared__ int wsum[4];
   __shared__ uint32_t cand_key[CAP];   // the top-digit bucket's keys and indices

@@ -67,11 +67,13 @@ def test_topk_tied_threshold_bucket():
     threshold bucket is larger than that (resolved over the row)."""
     say("topk tied threshold bucket")
     rng = np.random.default_rng(6)
-    T, N = 12, 9000
+    T, N = 14, 9000
     s = (-np.abs(rng.standard_normal((T, N))) - 3.0).astype(np.float32)
     for t in range(T):
-        n_tie = [2500, 2100, 3000, 2049, 6000, 9000][t % 6]
-        n_hi = [0, 500, 1000, 0, 100, 0][t % 6]
+        # bucket of the threshold score: 1500 .. 2000 keys (resolved in LDS)
+        # or 2049 / 6000 / 9000 keys (resolved over the row)
+        n_tie = [1800, 2000, 1700, 2049, 6000, 1500, 9000][t % 7]
+        n_hi = [500, 100, 1000, 0, 100, 700, 0][t % 7]
         pos = rng.permutation(N)
         s[t, pos[:n_tie]] = 1.0
         s[t, pos[n_tie:n_tie + n_hi]] = 2.0 + rng.random(n_hi).astype(np.float32)
