@@ -30,6 +30,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "smla_internal.h"
 
 namespace smla {
@@ -926,9 +928,8 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
       //             P of tile i exchanged (barrier)
       //             P.V of tile i       ||  V^T operands of tile i+1
       // Tile i's slot is free after step i-1 (its K and V^T were read then), so
-      // the gathers of step i refill it.  Every step issues one tile's gathers
-      // (past the list they re-read its last row into a free slot), which keeps
-      // the outstanding-load count fixed.
+      // the gathers of step i refill it.  Gathers stop at the last tile; the
+      // waits count the tiles actually in flight.
       constexpr int KRING = 8;
       const uint8_t* dg = a.kv;
       uint32_t dmb = 0;
@@ -1101,11 +1102,13 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
       if (nit > 0) {
 #pragma unroll
         for (int st = 0; st < S::NST; ++st) {
-          dma_prep(st);
+          if (st < nit) {
+            dma_prep(st);
 #pragma unroll
-          for (int L = 0; L < S::NLINES; ++L) dma_line(L);
+            for (int L = 0; L < S::NLINES; ++L) dma_line(L);
+          }
         }
-        wait_vm<(S::NST - 1) * S::PER>();
+        wait_tiles<S::PER, S::NST>((nit < S::NST ? nit : S::NST) - 1);   // tile 0 has landed
         lds_barrier();
         // P of tile i is published into exchange buffer i & 1 at the end of
         // step i - 1 (the prologue for tile 0); the barrier that opens step i
@@ -1130,8 +1133,17 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         bf16x8 vpre[8];
 #pragma unroll
         for (int f = 0; f < 8; ++f) vpre[f] = read_vt(0, f);
-        for (int it = 0; it < nit; ++it) {
-          wait_vm<(S::NST - 2) * S::PER>();   // tile it+1 has landed (this wave's share)
+        // step it; REFILL: the gathers of tile it + NST (all but the last NST
+        // steps), so those steps keep a full ring and wait on a constant count
+        auto step = [&](int it, auto refill_tag) {
+          constexpr bool REFILL = decltype(refill_tag)::value;
+          // tile it+1 has landed (this wave's share); tiles up to
+          // min(it + NST - 1, nit - 1) have been issued
+          if constexpr (REFILL) {
+            wait_vm<(S::NST - 2) * S::PER>();
+          } else {
+            if (it + 1 < nit) wait_tiles<S::PER, S::NST>(nit - it - 2 < S::NST - 2 ? nit - it - 2 : S::NST - 2);
+          }
           // every wave's reads of tile it (its V^T operands) have completed
           // before any gather refills that slot, and P of tile it is published
           asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -1149,7 +1161,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
           // the gathers of tile it + NST (into tile it's slot, free since the
           // last step) and the softmax of tile it+1 run under these MFMAs
           // (past the list the softmax sees only masked rows: no effect)
-          dma_prep(it + S::NST);
+          if constexpr (REFILL) dma_prep(it + S::NST);
           const bf16x8 pb = softmax(it + 1, scn, false);
 #pragma unroll
           for (int f = 0; f < 8; ++f) {
@@ -1157,11 +1169,14 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
             for (int hf = 0; hf < 4; ++hf)
               o[4 * f + hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vpre[f], pall[hf], o[4 * f + hf], 0, 0, 0);
             vpre[f] = read_vt(it + 1, f);
-            dma_line(f);
+            if constexpr (REFILL) dma_line(f);
           }
-          if constexpr (S::NLINES > 8) dma_line(8);
+          if constexpr (REFILL && S::NLINES > 8) dma_line(8);
           publish(pb, (it + 1) & 1);
-        }
+        };
+        int it = 0;
+        for (; it < nit - S::NST; ++it) step(it, std::true_type{});
+        for (; it < nit; ++it) step(it, std::false_type{});
       }
     } else {
       // ---- the pipeline
