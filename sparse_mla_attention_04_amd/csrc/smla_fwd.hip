@@ -43,6 +43,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 
 constexpr int D_QK = 576;
 constexpr int D_V = 512;
@@ -640,7 +641,6 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         for (int f = 0; f < S::NF; ++f) {
           // latent: 16 k-steps of 8 fp8 codes per lane, dequantised exactly to
           // bf16; each 128-dim block accumulates separately and is scaled in fp32
-          typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
           // 16 codes per lane per read: k-steps (b, 2m) and (b, 2m + 1) of block b
           u32x4 kq[8];
 #pragma unroll
@@ -1101,15 +1101,18 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
       };
 
       if (nit > 0) {
+        // (the row-half split variant issues a full ring even past the list:
+        // its steps wait on a constant count)
 #pragma unroll
         for (int st = 0; st < S::NST; ++st) {
-          if (st < nit) {
+          if (S::RSPLIT || st < nit) {
             dma_prep(st);
 #pragma unroll
             for (int L = 0; L < S::NLINES; ++L) dma_line(L);
           }
         }
-        wait_tiles<S::PER, S::NST>((nit < S::NST ? nit : S::NST) - 1);   // tile 0 has landed
+        if constexpr (S::RSPLIT) wait_vm<(S::NST - 1) * S::PER>();       // tile 0 has landed
+        else wait_tiles<S::PER, S::NST>((nit < S::NST ? nit : S::NST) - 1);
         lds_barrier();
         // P of tile i is published into exchange buffer i & 1 at the end of
         // step i - 1 (the prologue for tile 0); the barrier that opens step i
@@ -1276,12 +1279,52 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
     }
   }
   if constexpr (S::DSPLIT) {
-    // stage as if head group hf held all 32 output fragments (layout read below)
+    // one row stream: every wave writes its own output dims straight from
+    // its accumulators.  Lane (g4, n) holds, in fragment (f, head group hf),
+    // dims 128 * wave + 16f + 4 * g4 .. +3 of head (or dense slot) 16hf + n.
+    __syncthreads();   // the statistics are visible
+    const bool split = a.write_partials != 0;
 #pragma unroll
-    for (int f = 0; f < 8; ++f)
+    for (int hf = 0; hf < 4; ++hf) {
+      const int sa = S::RSPLIT ? 2 * hf : hf;   // statistics slot(s) of head group hf
+      const int m = 16 * hf + n;
+      const float M = stat[(sa * 16 + n) * 2];
+      const float L = (M != NEG_INF) ? stat[(sa * 16 + n) * 2 + 1] + (S::RSPLIT ? stat[((sa + 1) * 16 + n) * 2 + 1] : 0.f)
+                                     : 0.f;
+      const bool empty = !(L > 0.f);
+      const float inv = empty ? 0.f : 1.f / L;
+      const float lse_v = empty ? NEG_INF : (M + __log2f(L)) * LN2;
+      int orow = t, ohead = m;
+      bool ok = m < a.h;
+      if constexpr (S::DENSE) {
+        const int r = m / a.h;
+        ok = r < d_nr;
+        orow = d_r0 + r;
+        ohead = m - r * a.h;
+      }
+      if (!ok) continue;
 #pragma unroll
-      for (int hf = 0; hf < 4; ++hf)
-        (reinterpret_cast<f32x4*>(smem) + (size_t)hf * 32 * 64)[(8 * hg + f) * 64 + lane] = o[4 * f + hf];
+      for (int f = 0; f < 8; ++f) {
+        const int d0 = 128 * hg + 16 * f + 4 * g4;
+        const f32x4 v = o[4 * f + hf];
+        if (!split) {
+          u32x2 pk;
+          pk[0] = (uint32_t)f32_to_bf16_bits(v[0] * inv) | ((uint32_t)f32_to_bf16_bits(v[1] * inv) << 16);
+          pk[1] = (uint32_t)f32_to_bf16_bits(v[2] * inv) | ((uint32_t)f32_to_bf16_bits(v[3] * inv) << 16);
+          *reinterpret_cast<u32x2*>(a.out + (int64_t)orow * a.out_st + (int64_t)ohead * a.out_sh + d0) = pk;
+        } else {
+          f32x4 w;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) w[j] = v[j] * inv;
+          *reinterpret_cast<f32x4*>(a.ws_out + (unit * a.h + ohead) * D_V + d0) = w;
+        }
+      }
+      if (hg == 0 && g4 == 0) {
+        if (!split) a.lse[(int64_t)orow * a.lse_st + ohead] = lse_v;
+        else a.ws_lse[unit * a.h + ohead] = lse_v;
+      }
+    }
+    return;
   } else if constexpr (S::PAIR) {
     // the row stream's 32 fragments, staged where its first wave's would be
     f32x4* ost = reinterpret_cast<f32x4*>(smem) + (size_t)(rg * S::HG) * 32 * 64;

@@ -55,6 +55,19 @@ def test_mini_tilings_and_variants(h, tiling, variant):
     check(out, lse, *oracle(c), what="mini h=%d %s v%d" % (h, tiling, variant))
 
 
+@pytest.mark.parametrize("h,variant,topk", [(64, 0, 70), (64, 2, 70), (33, 2, 100), (48, 0, 100), (64, 0, 127),
+                                             (64, 2, 127), (64, 0, 129), (16, 0, 40)])
+def test_lists_shorter_than_the_tile_ring(h, variant, topk):
+    """Rows of one to four 32-row tiles: fewer tiles than the pipelined
+    kernels' ring holds, so their gathers and waits run the short-list paths."""
+    say("short lists", h, variant, topk)
+    c = G.make_mini(seed=31, num_heads=h, topk=topk, drop_frac=0.2)
+    dev = Dev(c)
+    for splits in (1, 2):
+        out, lse = to_np(*run_gpu(dev, variant=variant, num_splits=splits))
+        check(out, lse, *oracle(c), what="short lists h=%d v%d topk %d s%d" % (h, variant, topk, splits))
+
+
 @pytest.mark.parametrize("h,splits", [(8, 2), (8, 3), (8, 7), (16, 5), (32, 3), (64, 4), (8, 40)])
 def test_mini_forced_splits(h, splits):
     say("mini splits", h, splits)
