@@ -354,7 +354,7 @@ def main():
         "config": {"workload": wl_name, "entry": "sparse_mla_dense_fwd" if dense else "sparse_mla_fwd",
                    "num_tokens": T, "num_heads": h, "topk": case.topk,
                    "kv_format": case.kv_format, "page_size": case.page_size, "tiling": tiling,
-                   "num_splits": pl.num_splits, "kernel_variant": args.variant,
+                   "num_splits": pl.num_splits, "kernel_variant": pl.kernel_variant,
                    "gather_order": {1: "list", 2: "slot"}[pl.gather_order],
                    "grid": pl.grid, "threads": pl.threads},
         "gathered_GBps_per_step": round(gathered / (ms_per_step * 1e-3) / 1e9, 1),

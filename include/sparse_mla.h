@@ -142,7 +142,9 @@ typedef struct smla_params {
   int32_t tiling;              /* SMLA_TILING_*                                       */
   int32_t num_splits;          /* 0 = automatic; n >= 1 forces n KV splits per row    */
   int32_t kernel_variant;      /* 0 = default pipeline shape; 1 = alternative shape   */
-                               /* (bf16 any h; fp8 h <= 16); anything else ->         */
+                               /* (bf16 any h; fp8 h <= 16); 2 = bf16 only: h <= 16   */
+                               /* two work-groups per CU, 33..64 heads (or PAD64) the */
+                               /* row-half score split; anything else ->              */
                                /* SMLA_ERR_UNSUPPORTED.  A tuning knob, see smla_plan;*/
                                /* same results to tolerance.                          */
   int32_t gather_order;        /* SMLA_GATHER_*: order in which a row's listed cache  */
@@ -167,6 +169,10 @@ typedef struct smla_plan {
   int32_t lds_bytes;           /* LDS per work-group                                  */
   int32_t num_cus;             /* compute units assumed by the plan                   */
   int32_t gather_order;        /* resolved SMLA_GATHER_LIST or SMLA_GATHER_SLOT        */
+  int32_t kernel_variant;      /* resolved kernel shape: the requested variant, or   */
+                               /* for variant 0 the shape the plan picks (2 for      */
+                               /* unsplit bf16 batches at h <= 16 of >= 2 rows per   */
+                               /* CU)                                                */
 } smla_plan;
 
 /* Bytes of workspace sparse_mla_fwd needs for calls described by *p.

@@ -60,7 +60,7 @@ class Plan(ctypes.Structure):
         ("workspace_bytes", ctypes.c_int64), ("partials_bytes", ctypes.c_int64),
         ("lds_bytes", ctypes.c_int32),
         ("num_cus", ctypes.c_int32),
-        ("gather_order", ctypes.c_int32),
+        ("gather_order", ctypes.c_int32), ("kernel_variant", ctypes.c_int32),
     ]
 
     def as_dict(self):

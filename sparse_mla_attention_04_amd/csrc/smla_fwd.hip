@@ -57,7 +57,7 @@ constexpr float LN2 = 0.69314718055994530942f;
 constexpr float REF_HEADROOM = 64.0f;   // p = 2^(x - ref) may reach 2^64 before a second pass is forced
 
 template <int HG_, int NRG_, int RT_, int NST_, int FMT_, bool DSPLIT_ = false, bool PIPE_ = false,
-          bool PAIR_ = false, bool RSPLIT_ = false, bool NOPE_ = false, bool DENSE_ = false>
+          bool PAIR_ = false, bool RSPLIT_ = false, bool NOPE_ = false, bool DENSE_ = false, bool TWO_ = false>
 struct Shape {
   static constexpr int HG = HG_;            // 16-head groups (waves per row group)
   static constexpr int NRG = NRG_;          // row groups (independent KV row streams)
@@ -79,7 +79,14 @@ struct Shape {
   static constexpr int PER = NLINES * RH_PER_WAVE + (FP8 ? 1 : 0);  // DMA instructions per wave per tile
   static constexpr int RING_BYTES = NRG * NST * TILE_BYTES;
   static constexpr int LIST_OFF = RING_BYTES;
-  static constexpr int CNT_OFF = LIST_OFF + LIST_CAP * 4;
+  // TWO: at most 80 KB of LDS, so two work-groups share a CU and one's
+  // start-up and epilogue overlap the other's tiles.  The compaction counts
+  // and the epilogue statistics then live in the tile ring, which is idle
+  // whenever they are used (before the first gather of a pass, after the
+  // last tile has been consumed).
+  static constexpr bool TWO = TWO_;
+  static constexpr int TWO_STAT_OFF = HG * NRG * 32 * 64 * 16;   // above the epilogue staging
+  static constexpr int CNT_OFF = TWO ? TWO_STAT_OFF + HG * NRG * 16 * 2 * 4 : LIST_OFF + LIST_CAP * 4;
   // DSPLIT: every wave computes P for its 16 heads, the waves exchange P
   // through LDS, and wave w accumulates output dims [128w, 128w + 128) for all
   // 4 head groups, so each V element is read from LDS once per tile.
@@ -108,10 +115,11 @@ struct Shape {
   static constexpr int PEX_OFF = PIPE ? CNT_OFF : CNT_OFF + 512;
   static constexpr int PEX_BYTES = DSPLIT ? 2 * 4 * 64 * 16 : PAIR ? NRG * 4 * 64 * 16 : 0;
   static constexpr int MEX_OFF = PEX_OFF + PEX_BYTES;
-  static constexpr int STAT_OFF = PIPE ? CNT_OFF : MEX_OFF + (PAIR ? NW * 64 * 4 : 0);
+  static constexpr int STAT_OFF = TWO ? TWO_STAT_OFF : PIPE ? CNT_OFF : MEX_OFF + (PAIR ? NW * 64 * 4 : 0);
   static constexpr int LDS_BYTES =
-      PIPE ? CNT_OFF + (PEX_BYTES > STAT_BYTES ? (PEX_BYTES > 512 ? PEX_BYTES : 512) : (STAT_BYTES > 512 ? STAT_BYTES : 512))
-           : STAT_OFF + STAT_BYTES;
+      TWO    ? LIST_OFF + LIST_CAP * 4
+      : PIPE ? CNT_OFF + (PEX_BYTES > STAT_BYTES ? (PEX_BYTES > 512 ? PEX_BYTES : 512) : (STAT_BYTES > 512 ? STAT_BYTES : 512))
+             : STAT_OFF + STAT_BYTES;
   static constexpr int EPT = LIST_CAP / NTHR;   // index entries per thread per pass
   static constexpr bool SYNC = HG > 1;          // waves share tiles -> barrier per tile
   static_assert(RT == 16 || RT == 32, "tile rows");
@@ -136,6 +144,8 @@ struct Shape {
   static_assert(!DSPLIT || PIPE, "the output-dim split runs in the pipelined schedule");
   static_assert(!PAIR || (FP8 && HG == 2 && RT == 32 && !DSPLIT), "row/dim-split pair layout");
   static_assert(!RSPLIT || PIPE, "the row-half score split runs in the pipelined schedule");
+  static_assert(!TWO || (!PIPE && !PAIR && !FP8 && NE == 1), "two-per-CU layout: plain bf16 row streams");
+  static_assert(!TWO || (CNT_OFF + NW * 8 * 4 <= RING_BYTES && LDS_BYTES <= 80 * 1024), "two-per-CU layout");
 };
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -1471,6 +1481,7 @@ __global__ void __launch_bounds__(256) smla_lse_combine(CombineArgs a) {
 // Kernel variants: (head groups, row groups, tile rows, stages, format).
 using V_H1_A = Shape<1, 4, 16, 2, 0>;
 using V_H1_B = Shape<1, 2, 16, 4, 0>;
+using V_H1_T = Shape<1, 2, 16, 2, 0, false, false, false, false, false, false, true>;   // two per CU
 using V_H2_A = Shape<2, 2, 32, 2, 0>;
 using V_H2_B = Shape<2, 1, 32, 4, 0>;
 using V_H4_A = Shape<4, 1, 32, 4, 0, true, true>;
@@ -1521,7 +1532,9 @@ bool fwd_shape(int kv_format, int head_groups, int variant, int nope, FwdShape* 
     }
   }
   switch (head_groups) {
-    case 1: *shape = variant == 1 ? shape_of<V_H1_B>() : shape_of<V_H1_A>(); return variant <= 1;
+    case 1:
+      *shape = variant == 2 ? shape_of<V_H1_T>() : variant == 1 ? shape_of<V_H1_B>() : shape_of<V_H1_A>();
+      return variant <= 2;
     case 2: *shape = variant == 1 ? shape_of<V_H2_B>() : shape_of<V_H2_A>(); return variant <= 1;
     case 4:
       *shape = variant == 2 ? shape_of<V_H4_C>() : variant == 1 ? shape_of<V_H4_B>() : shape_of<V_H4_A>();
@@ -1549,7 +1562,10 @@ hipError_t launch_fwd(const FwdArgs& a, int kv_format, int head_groups, int vari
     }
   }
   switch (head_groups) {
-    case 1: return variant == 1 ? launch_one<V_H1_B>(a, grid, stream) : launch_one<V_H1_A>(a, grid, stream);
+    case 1:
+      return variant == 2   ? launch_one<V_H1_T>(a, grid, stream)
+             : variant == 1 ? launch_one<V_H1_B>(a, grid, stream)
+                            : launch_one<V_H1_A>(a, grid, stream);
     case 2: return variant == 1 ? launch_one<V_H2_B>(a, grid, stream) : launch_one<V_H2_A>(a, grid, stream);
     case 4:
       return variant == 2   ? launch_one<V_H4_C>(a, grid, stream)

@@ -69,7 +69,8 @@ def test_zero_tokens_is_noop():
     (dict(kernel_variant=7), B.SMLA_ERR_UNSUPPORTED),
     (dict(kernel_variant=1, kv_format="fp8", num_heads=32), B.SMLA_ERR_UNSUPPORTED),
     (dict(kernel_variant=2, kv_format="fp8"), B.SMLA_ERR_UNSUPPORTED),
-    (dict(kernel_variant=2), B.SMLA_ERR_UNSUPPORTED),                 # h = 8: no third shape
+    (dict(kernel_variant=2, num_heads=32), B.SMLA_ERR_UNSUPPORTED),   # 17..32 heads: no third shape
+    (dict(kernel_variant=2, geometry="nope"), B.SMLA_ERR_UNSUPPORTED),
     (dict(kernel_variant=3, num_heads=64), B.SMLA_ERR_UNSUPPORTED),
     (dict(geometry="nope", kv_format="fp8"), B.SMLA_ERR_UNSUPPORTED),     # NoPE: bf16 caches only
     (dict(geometry="nope", kernel_variant=1), B.SMLA_ERR_UNSUPPORTED),    # NoPE: default shapes only
@@ -186,6 +187,14 @@ def test_plan_for_is_pure_and_splits_small_batches():
     assert pl.num_splits == 5 and pl.units == 250 and pl.grid == 256
     pl = B.plan(_params(num_tokens=20, topk=256, num_heads=64), num_cus=256)
     assert pl.num_splits == 8 and pl.units == 160 and pl.grid == 160
+    # unsplit bf16 batches at h <= 16 with >= 2 rows per CU: the two-per-CU shape
+    pl = B.plan(_params(num_tokens=4096, topk=2048, num_heads=8), num_cus=256)
+    assert pl.kernel_variant == 2 and pl.threads == 128 and pl.lds_bytes <= 80 * 1024 and pl.row_groups == 2
+    assert B.plan(_params(num_tokens=511, topk=2048, num_heads=8), num_cus=256).kernel_variant == 0
+    assert B.plan(_params(num_tokens=32, topk=2048, num_heads=8), num_cus=256).kernel_variant == 0
+    assert B.plan(_params(num_tokens=4096, topk=2048, num_heads=32), num_cus=256).kernel_variant == 0
+    assert B.plan(_params(num_tokens=4096, topk=2048, num_heads=8, kernel_variant=1), num_cus=256).kernel_variant == 1
+    assert B.plan(_params(num_tokens=4096, topk=2048, num_heads=8, kv_format="fp8"), num_cus=256).kernel_variant == 0
     # one head group: every split keeps at least 256 list entries
     assert B.plan(_params(num_tokens=64, topk=128, num_heads=8), num_cus=256).num_splits == 1
     assert B.plan(_params(num_tokens=64, topk=512, num_heads=8), num_cus=256).num_splits == 2

@@ -393,6 +393,41 @@ def test_c3_sweep_sampled(c3_case, c3_dev, h, tiling):
     check(out[rows], lse[rows], ref_o, ref_l, "c3 h=%d %s" % (h, tiling))
 
 
+@pytest.mark.parametrize("h", [8, 16])
+def test_c3_two_per_cu_shape_sampled(c3_case, c3_dev, h):
+    """The h <= 16 shape that fits two work-groups per CU (variant 2) on the
+    4096-row sweep."""
+    say("c3 two-per-CU", h)
+    out, lse = to_np(*run_gpu(c3_dev, heads=h, variant=2))
+    rows = _sample_rows(c3_case, 24, seed=h + 100)
+    ref_o, ref_l = oracle(c3_case, rows=rows, heads=h)
+    check(out[rows], lse[rows], ref_o, ref_l, "c3 h=%d two-per-CU" % h)
+
+
+@pytest.mark.parametrize("h,splits,topk", [(1, 1, 300), (8, 1, 300), (12, 3, 300), (16, 1, 5000), (8, 2, 40),
+                                           (16, 1, 17)])
+def test_two_per_cu_shape_mini(h, splits, topk):
+    """Variant 2 at h <= 16 (two row streams, 80 KB of LDS, the compaction
+    counts and statistics inside the idle tile ring): ragged tails, -1 holes,
+    forced splits, two compaction passes (top-k 5000), lists shorter than one
+    tile per stream."""
+    say("two-per-CU mini", h, splits, topk)
+    c = G.make_mini(seed=41, num_heads=h, topk=topk, drop_frac=0.2)
+    dev = Dev(c)
+    out, lse = to_np(*run_gpu(dev, variant=2, num_splits=splits))
+    check(out, lse, *oracle(c), what="two-per-CU h=%d s%d topk %d" % (h, splits, topk))
+    o0, l0 = to_np(*run_gpu(dev, variant=0, num_splits=splits))
+    assert np.abs(lse - l0).max() <= SPLIT_ATOL
+
+
+def test_c2_decode_two_per_cu_shape():
+    say("c2 two-per-CU")
+    c = G.make_config("c2_decode")
+    dev = Dev(c)
+    out, lse = to_np(*run_gpu(dev, variant=2))
+    check(out, lse, *oracle(c), what="c2 two-per-CU")
+
+
 def test_c4_long_prefill_sampled():
     say("c4")
     c = G.make_config("c4_long_prefill")
