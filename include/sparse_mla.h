@@ -98,7 +98,8 @@ extern "C" {
 
 /* geometry (smla_params.geometry): the width of query heads and cache rows.
  * MLA: 576 = 512 latent + 64 rope dims.  NOPE: 512 latent dims, no rope
- * part (bf16 caches, kernel_variant 0; anything else -> SMLA_ERR_UNSUPPORTED).
+ * part (bf16 caches, kernel_variant 0, or 2 at h <= 32; anything else ->
+ * SMLA_ERR_UNSUPPORTED).
  * The output is 512 wide either way.  0 is MLA, so zero-initialised params
  * keep the rope part. */
 #define SMLA_GEOM_MLA 0
@@ -141,12 +142,13 @@ typedef struct smla_params {
   float softmax_scale;         /* multiplies q.k (e.g. 1/sqrt(576)); finite           */
   int32_t tiling;              /* SMLA_TILING_*                                       */
   int32_t num_splits;          /* 0 = automatic; n >= 1 forces n KV splits per row    */
-  int32_t kernel_variant;      /* 0 = default pipeline shape; 1 = alternative shape   */
-                               /* (bf16 any h; fp8 h <= 16); 2 = bf16 only: h <= 16   */
-                               /* two work-groups per CU, 33..64 heads (or PAD64) the */
-                               /* row-half score split; anything else ->              */
-                               /* SMLA_ERR_UNSUPPORTED.  A tuning knob, see smla_plan;*/
-                               /* same results to tolerance.                          */
+  int32_t kernel_variant;      /* 0 = default (the plan picks the shape); 1 = the     */
+                               /* alternative shape (bf16 MLA any h; fp8 h <= 16);    */
+                               /* 2 = two work-groups per CU at h <= 32 (bf16, MLA or */
+                               /* NoPE) or h <= 16 (fp8), and at 33..64 heads (or     */
+                               /* PAD64, bf16 MLA) the row-half score split; anything */
+                               /* else -> SMLA_ERR_UNSUPPORTED.  A tuning knob, see   */
+                               /* smla_plan; same results to tolerance.               */
   int32_t gather_order;        /* SMLA_GATHER_*: order in which a row's listed cache  */
                                /* rows are gathered (the result is the same set sum;  */
                                /* fp32 summation order, hence rounding, follows it)   */
@@ -171,8 +173,8 @@ typedef struct smla_plan {
   int32_t gather_order;        /* resolved SMLA_GATHER_LIST or SMLA_GATHER_SLOT        */
   int32_t kernel_variant;      /* resolved kernel shape: the requested variant, or   */
                                /* for variant 0 the shape the plan picks (2 for      */
-                               /* unsplit bf16 batches at h <= 16 of >= 2 rows per   */
-                               /* CU)                                                */
+                               /* unsplit batches of >= 2 rows per CU at h <= 32     */
+                               /* bf16 or h <= 16 fp8, else 0)                       */
 } smla_plan;
 
 /* Bytes of workspace sparse_mla_fwd needs for calls described by *p.

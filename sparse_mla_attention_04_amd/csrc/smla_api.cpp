@@ -114,16 +114,18 @@ int make_plan(const smla_params* p, int32_t num_cus, smla_plan* plan) {
   if (!smla::fwd_shape(p->kv_format, hg, p->kernel_variant, p->geometry == SMLA_GEOM_NOPE, &sh))
     return SMLA_ERR_UNSUPPORTED;
   const int S = splits_for(p, num_cus, sh);
-  // Unsplit bf16 batches at h <= 16 with at least two rows per CU run the
-  // shape that fits two work-groups on a CU (kernel variant 2): one row's
-  // start-up and epilogue overlap another's tiles.  Measured on MI355X, 4096
-  // rows of 2048 entries: h = 8 714 -> 656 us, h = 16 758 -> 672 us; 64 rows
-  // (one per CU) ran 13.4 -> 15.6 us, hence the row threshold.
+  // Unsplit batches with at least two rows per CU run, at h <= 32 (bf16) or
+  // h <= 16 (fp8), the shapes that fit two work-groups on a CU (kernel
+  // variant 2): one row's start-up and epilogue overlap another's tiles.
+  // Measured on MI355X, rows of 2048 entries: 4096 rows at h = 8 714 -> 656
+  // us, h = 16 758 -> 672 us, h = 32 1057 -> 853 us; 32768 fp8 rows at h = 8
+  // 7050 -> 6532 us; 64 rows (one per CU) ran 13.4 -> 15.6 us, hence the row
+  // threshold.
   int variant = p->kernel_variant;
-  if (variant == 0 && S == 1 && hg == 1 && p->kv_format == SMLA_KV_BF16 && p->geometry != SMLA_GEOM_NOPE &&
-      p->num_tokens >= 2 * (int64_t)num_cus) {
+  if (variant == 0 && S == 1 && p->num_tokens >= 2 * (int64_t)num_cus &&
+      (p->kv_format == SMLA_KV_BF16 ? hg <= 2 : hg == 1)) {
     variant = 2;
-    if (!smla::fwd_shape(p->kv_format, hg, variant, 0, &sh)) return SMLA_ERR_UNSUPPORTED;
+    if (!smla::fwd_shape(p->kv_format, hg, variant, p->geometry == SMLA_GEOM_NOPE, &sh)) return SMLA_ERR_UNSUPPORTED;
   }
   smla_plan pl{};
   pl.kernel_variant = variant;

@@ -1484,6 +1484,7 @@ using V_H1_B = Shape<1, 2, 16, 4, 0>;
 using V_H1_T = Shape<1, 2, 16, 2, 0, false, false, false, false, false, false, true>;   // two per CU
 using V_H2_A = Shape<2, 2, 32, 2, 0>;
 using V_H2_B = Shape<2, 1, 32, 4, 0>;
+using V_H2_T = Shape<2, 1, 32, 2, 0, false, false, false, false, false, false, true>;   // two per CU
 using V_H4_A = Shape<4, 1, 32, 4, 0, true, true>;
 using V_H4_B = Shape<4, 1, 32, 4, 0>;
 using V_H4_C = Shape<4, 1, 32, 4, 0, true, true, false, true>;
@@ -1491,11 +1492,15 @@ using V_H4_C = Shape<4, 1, 32, 4, 0, true, true, false, true>;
 using N_H1_A = Shape<1, 4, 16, 2, 0, false, false, false, false, true>;
 using N_H2_A = Shape<2, 2, 32, 2, 0, false, false, false, false, true>;
 using N_H4_A = Shape<4, 1, 32, 4, 0, true, true, false, false, true>;
+// NoPE, two work-groups per CU (the 1 KB rows leave room for the usual layout)
+using N_H1_T = Shape<1, 2, 16, 2, 0, false, false, false, false, true>;
+using N_H2_T = Shape<2, 1, 32, 2, 0, false, false, false, false, true>;
 // dense causal mode (576- and 512-wide rows)
 using D_H4 = Shape<4, 1, 32, 4, 0, true, true, false, false, false, true>;
 using D_H4_N = Shape<4, 1, 32, 4, 0, true, true, false, false, true, true>;
 using F_H1_A = Shape<2, 2, 32, 3, 1, false, false, true>;
 using F_H1_B = Shape<1, 2, 32, 3, 1>;
+using F_H1_T = Shape<2, 1, 32, 3, 1, false, false, true>;   // one wave-pair stream: two per CU
 using F_H2_A = Shape<2, 1, 32, 4, 1>;
 using F_H4_A = Shape<4, 1, 32, 7, 1>;
 
@@ -1514,18 +1519,20 @@ hipError_t launch_one(const FwdArgs& a, int64_t grid, hipStream_t stream) {
 
 bool fwd_shape(int kv_format, int head_groups, int variant, int nope, FwdShape* shape) {
   if (nope) {
-    if (kv_format != 0 || variant != 0) return false;
+    if (kv_format != 0 || !(variant == 0 || (variant == 2 && head_groups <= 2))) return false;
     switch (head_groups) {
-      case 1: *shape = shape_of<N_H1_A>(); return true;
-      case 2: *shape = shape_of<N_H2_A>(); return true;
+      case 1: *shape = variant == 2 ? shape_of<N_H1_T>() : shape_of<N_H1_A>(); return true;
+      case 2: *shape = variant == 2 ? shape_of<N_H2_T>() : shape_of<N_H2_A>(); return true;
       case 4: *shape = shape_of<N_H4_A>(); return true;
       default: return false;
     }
   }
   if (kv_format == 1) {
-    if (variant != 0 && !(variant == 1 && head_groups == 1)) return false;
+    if (variant != 0 && !((variant == 1 || variant == 2) && head_groups == 1)) return false;
     switch (head_groups) {
-      case 1: *shape = variant == 1 ? shape_of<F_H1_B>() : shape_of<F_H1_A>(); return true;
+      case 1:
+        *shape = variant == 2 ? shape_of<F_H1_T>() : variant == 1 ? shape_of<F_H1_B>() : shape_of<F_H1_A>();
+        return true;
       case 2: *shape = shape_of<F_H2_A>(); return true;
       case 4: *shape = shape_of<F_H4_A>(); return true;
       default: return false;
@@ -1535,7 +1542,9 @@ bool fwd_shape(int kv_format, int head_groups, int variant, int nope, FwdShape* 
     case 1:
       *shape = variant == 2 ? shape_of<V_H1_T>() : variant == 1 ? shape_of<V_H1_B>() : shape_of<V_H1_A>();
       return variant <= 2;
-    case 2: *shape = variant == 1 ? shape_of<V_H2_B>() : shape_of<V_H2_A>(); return variant <= 1;
+    case 2:
+      *shape = variant == 2 ? shape_of<V_H2_T>() : variant == 1 ? shape_of<V_H2_B>() : shape_of<V_H2_A>();
+      return variant <= 2;
     case 4:
       *shape = variant == 2 ? shape_of<V_H4_C>() : variant == 1 ? shape_of<V_H4_B>() : shape_of<V_H4_A>();
       return variant <= 2;
@@ -1547,15 +1556,18 @@ hipError_t launch_fwd(const FwdArgs& a, int kv_format, int head_groups, int vari
                       hipStream_t stream) {
   if (nope) {
     switch (head_groups) {
-      case 1: return launch_one<N_H1_A>(a, grid, stream);
-      case 2: return launch_one<N_H2_A>(a, grid, stream);
+      case 1: return variant == 2 ? launch_one<N_H1_T>(a, grid, stream) : launch_one<N_H1_A>(a, grid, stream);
+      case 2: return variant == 2 ? launch_one<N_H2_T>(a, grid, stream) : launch_one<N_H2_A>(a, grid, stream);
       case 4: return launch_one<N_H4_A>(a, grid, stream);
       default: return hipErrorInvalidValue;
     }
   }
   if (kv_format == 1) {
     switch (head_groups) {
-      case 1: return variant == 1 ? launch_one<F_H1_B>(a, grid, stream) : launch_one<F_H1_A>(a, grid, stream);
+      case 1:
+        return variant == 2   ? launch_one<F_H1_T>(a, grid, stream)
+               : variant == 1 ? launch_one<F_H1_B>(a, grid, stream)
+                              : launch_one<F_H1_A>(a, grid, stream);
       case 2: return launch_one<F_H2_A>(a, grid, stream);
       case 4: return launch_one<F_H4_A>(a, grid, stream);
       default: return hipErrorInvalidValue;
@@ -1566,7 +1578,10 @@ hipError_t launch_fwd(const FwdArgs& a, int kv_format, int head_groups, int vari
       return variant == 2   ? launch_one<V_H1_T>(a, grid, stream)
              : variant == 1 ? launch_one<V_H1_B>(a, grid, stream)
                             : launch_one<V_H1_A>(a, grid, stream);
-    case 2: return variant == 1 ? launch_one<V_H2_B>(a, grid, stream) : launch_one<V_H2_A>(a, grid, stream);
+    case 2:
+      return variant == 2   ? launch_one<V_H2_T>(a, grid, stream)
+             : variant == 1 ? launch_one<V_H2_B>(a, grid, stream)
+                            : launch_one<V_H2_A>(a, grid, stream);
     case 4:
       return variant == 2   ? launch_one<V_H4_C>(a, grid, stream)
              : variant == 1 ? launch_one<V_H4_B>(a, grid, stream)

@@ -68,9 +68,9 @@ def test_zero_tokens_is_noop():
     (dict(kernel_variant=-1), B.SMLA_ERR_INVALID_ARG),
     (dict(kernel_variant=7), B.SMLA_ERR_UNSUPPORTED),
     (dict(kernel_variant=1, kv_format="fp8", num_heads=32), B.SMLA_ERR_UNSUPPORTED),
-    (dict(kernel_variant=2, kv_format="fp8"), B.SMLA_ERR_UNSUPPORTED),
-    (dict(kernel_variant=2, num_heads=32), B.SMLA_ERR_UNSUPPORTED),   # 17..32 heads: no third shape
-    (dict(kernel_variant=2, geometry="nope"), B.SMLA_ERR_UNSUPPORTED),
+    (dict(kernel_variant=2, kv_format="fp8", num_heads=32), B.SMLA_ERR_UNSUPPORTED),
+    (dict(kernel_variant=3, num_heads=32), B.SMLA_ERR_UNSUPPORTED),
+    (dict(kernel_variant=2, geometry="nope", num_heads=64), B.SMLA_ERR_UNSUPPORTED),
     (dict(kernel_variant=3, num_heads=64), B.SMLA_ERR_UNSUPPORTED),
     (dict(geometry="nope", kv_format="fp8"), B.SMLA_ERR_UNSUPPORTED),     # NoPE: bf16 caches only
     (dict(geometry="nope", kernel_variant=1), B.SMLA_ERR_UNSUPPORTED),    # NoPE: default shapes only
@@ -192,9 +192,14 @@ def test_plan_for_is_pure_and_splits_small_batches():
     assert pl.kernel_variant == 2 and pl.threads == 128 and pl.lds_bytes <= 80 * 1024 and pl.row_groups == 2
     assert B.plan(_params(num_tokens=511, topk=2048, num_heads=8), num_cus=256).kernel_variant == 0
     assert B.plan(_params(num_tokens=32, topk=2048, num_heads=8), num_cus=256).kernel_variant == 0
-    assert B.plan(_params(num_tokens=4096, topk=2048, num_heads=32), num_cus=256).kernel_variant == 0
+    assert B.plan(_params(num_tokens=4096, topk=2048, num_heads=32), num_cus=256).kernel_variant == 2
+    assert B.plan(_params(num_tokens=4096, topk=2048, num_heads=64), num_cus=256).kernel_variant == 0
     assert B.plan(_params(num_tokens=4096, topk=2048, num_heads=8, kernel_variant=1), num_cus=256).kernel_variant == 1
-    assert B.plan(_params(num_tokens=4096, topk=2048, num_heads=8, kv_format="fp8"), num_cus=256).kernel_variant == 0
+    pf = B.plan(_params(num_tokens=4096, topk=2048, num_heads=8, kv_format="fp8"), num_cus=256)
+    assert pf.kernel_variant == 2 and pf.threads == 128 and pf.lds_bytes <= 80 * 1024
+    assert B.plan(_params(num_tokens=4096, topk=2048, num_heads=32, kv_format="fp8"), num_cus=256).kernel_variant == 0
+    pn = B.plan(_params(num_tokens=4096, topk=2048, num_heads=8, geometry="nope"), num_cus=256)
+    assert pn.kernel_variant == 2 and pn.lds_bytes <= 80 * 1024
     # one head group: every split keeps at least 256 list entries
     assert B.plan(_params(num_tokens=64, topk=128, num_heads=8), num_cus=256).num_splits == 1
     assert B.plan(_params(num_tokens=64, topk=512, num_heads=8), num_cus=256).num_splits == 2
@@ -204,9 +209,12 @@ def test_plan_for_is_pure_and_splits_small_batches():
     assert B.plan(_params(num_heads=64), num_cus=256).head_groups == 4
     assert B.plan(_params(num_heads=8, tiling="pad64"), num_cus=256).head_groups == 4
     # fp8, h <= 16: one head group, two row streams of two waves each (the
-    # launch dispatches on the plan's head-group count)
+    # launch dispatches on the plan's head-group count); for >= 2 rows per
+    # CU one stream of two waves, two work-groups per CU
+    pf = B.plan(_params(num_heads=8, kv_format="fp8", num_tokens=256, topk=2048), num_cus=256)
+    assert pf.head_groups == 1 and pf.row_groups == 2 and pf.threads == 256 and pf.kernel_variant == 0
     pf = B.plan(_params(num_heads=8, kv_format="fp8", num_tokens=4096, topk=2048), num_cus=256)
-    assert pf.head_groups == 1 and pf.row_groups == 2 and pf.threads == 256
+    assert pf.head_groups == 1 and pf.row_groups == 1 and pf.threads == 128 and pf.kernel_variant == 2
     pf1 = B.plan(_params(num_heads=8, kv_format="fp8", kernel_variant=1), num_cus=256)
     assert pf1.head_groups == 1 and pf1.threads == 128
     # grid is a multiple of 8 (XCD-aware mapping)

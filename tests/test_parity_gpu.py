@@ -420,6 +420,37 @@ def test_two_per_cu_shape_mini(h, splits, topk):
     assert np.abs(lse - l0).max() <= SPLIT_ATOL
 
 
+@pytest.mark.parametrize("h,kv_format,splits,topk", [(24, "bf16", 1, 300), (32, "bf16", 3, 300), (17, "bf16", 1, 5000),
+                                                     (32, "bf16", 1, 20), (8, "fp8", 1, 300), (16, "fp8", 3, 333),
+                                                     (12, "fp8", 1, 5000), (8, "fp8", 1, 40)])
+def test_two_per_cu_shapes_h32_and_fp8(h, kv_format, splits, topk):
+    """Variant 2 at 17..32 heads (one stream of two head-group waves, 80 KB
+    of LDS) and for fp8 at h <= 16 (one wave-pair stream, 75 KB)."""
+    say("two-per-CU", h, kv_format, splits, topk)
+    c = G.make_mini(seed=43, num_heads=h, topk=topk, kv_format=kv_format, drop_frac=0.2)
+    dev = Dev(c)
+    out, lse = to_np(*run_gpu(dev, variant=2, num_splits=splits))
+    check(out, lse, *oracle(c), what="two-per-CU h=%d %s s%d topk %d" % (h, kv_format, splits, topk))
+
+
+@pytest.mark.parametrize("h", [32])
+def test_c3_two_per_cu_h32_sampled(c3_case, c3_dev, h):
+    say("c3 two-per-CU", h)
+    out, lse = to_np(*run_gpu(c3_dev, heads=h, variant=2))
+    rows = _sample_rows(c3_case, 24, seed=h + 200)
+    ref_o, ref_l = oracle(c3_case, rows=rows, heads=h)
+    check(out[rows], lse[rows], ref_o, ref_l, "c3 h=%d two-per-CU" % h)
+
+
+def test_c5_fp8_two_per_cu_sampled():
+    say("c5 fp8 two-per-CU")
+    c = G.make_config("c5_fp8")
+    dev = Dev(c)
+    out, lse = to_np(*run_gpu(dev, variant=2))
+    rows = _sample_rows(c, 48, seed=55)
+    check(out[rows], lse[rows], *oracle(c, rows=rows), what="c5 two-per-CU")
+
+
 def test_c2_decode_two_per_cu_shape():
     say("c2 two-per-CU")
     c = G.make_config("c2_decode")
@@ -603,6 +634,15 @@ def test_nope_mini(h, tiling, splits):
     c = G.make_mini(seed=71, num_heads=h, topk=300, rope_dims=0)
     out, lse = to_np(*run_gpu(Dev(c), tiling=tiling, num_splits=splits))
     check(out, lse, *oracle(c), what="nope h=%d %s s%d" % (h, tiling, splits))
+
+
+@pytest.mark.parametrize("h,splits,topk", [(8, 1, 300), (16, 3, 300), (24, 1, 5000), (32, 1, 20)])
+def test_nope_two_per_cu_shapes(h, splits, topk):
+    """NoPE rows with the two-work-groups-per-CU shapes (variant 2)."""
+    say("nope two-per-CU", h, splits, topk)
+    c = G.make_mini(seed=74, num_heads=h, topk=topk, rope_dims=0, drop_frac=0.2)
+    out, lse = to_np(*run_gpu(Dev(c), variant=2, num_splits=splits))
+    check(out, lse, *oracle(c), what="nope two-per-CU h=%d s%d topk %d" % (h, splits, topk))
 
 
 def test_nope_slot_mode_and_orders_bit_identical():
