@@ -356,7 +356,11 @@ def main():
                    "kv_format": case.kv_format, "page_size": case.page_size, "tiling": tiling,
                    "num_splits": pl.num_splits, "kernel_variant": pl.kernel_variant,
                    "gather_order": {1: "list", 2: "slot"}[pl.gather_order],
-                   "grid": pl.grid, "threads": pl.threads},
+                   "grid": pl.grid, "threads": pl.threads} if not dense else
+                  {"workload": wl_name, "entry": "sparse_mla_dense_fwd", "num_tokens": T, "num_heads": h,
+                   "kv_format": case.kv_format, "page_size": case.page_size,
+                   "rows_per_work_group": 64 // h, "kernel": "pipelined h=64 schedule, (row, head) query slots",
+                   "grid": ((T + 64 // h - 1) // (64 // h) + case.block_table.shape[0] + 7) // 8 * 8, "threads": 256},
         "gathered_GBps_per_step": round(gathered / (ms_per_step * 1e-3) / 1e9, 1),
         "mfma_frac_per_step": round(flops / (ms_per_step * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 5),
         "wall_s_timed": round(wall, 4),
