@@ -79,3 +79,13 @@ def test_topk_tied_threshold_bucket():
         s[t, pos[n_tie:n_tie + n_hi]] = 2.0 + rng.random(n_hi).astype(np.float32)
     _check(s, None, 2048)
     _check(s, rng.integers(2049, N + 1, size=T), 2048)
+
+
+def test_topk_rows_longer_than_65536_keys():
+    """Rows longer than the long-prefill history, one with a tied threshold
+    bucket larger than the LDS copy."""
+    say("topk rows > 65536 keys")
+    rng = np.random.default_rng(7)
+    s = rng.standard_normal((6, 70004)).astype(np.float32)
+    s[1, :40000] = 0.5                     # a tied threshold bucket larger than the LDS copy
+    _check(s, [70004, 65537, 70000, 3000, 0, 69999], 2048)
