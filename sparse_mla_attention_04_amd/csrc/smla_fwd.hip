@@ -26,7 +26,10 @@
 //     end; a split work-group writes its fp32 partial (normalised output
 //     and lse) to the caller's workspace instead, and a second kernel merges
 //     the splits by their lse (the fp32 split-KV path of PR #60220,
-//     "Overview"/"Limitations", with the buffer owned by the caller).
+//     "Overview"/"Limitations", with the buffer owned by the caller);
+//   * at up to 32 heads, shapes of two waves and at most 80 KB of LDS let two
+//     work-groups share a CU, so one row's start-up loads and epilogue
+//     overlap another row's tiles.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -1345,10 +1348,11 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
 #pragma unroll
     for (int f = 0; f < 32; ++f) ost[f * 64 + lane] = o[f];
   }
+  // (only shapes without the output-dim split reach here: one query row per
+  // work-group, row streams merged through LDS)
   __syncthreads();
   const bool split = a.write_partials != 0;
-  // (dense mode: `head` is the query slot m = row * h + head of the block)
-  const int n_items = (S::DENSE ? d_nr : 1) * a.h * 64;
+  const int n_items = a.h * 64;
   // unrolled so the LDS reads of several items are in flight together
 #pragma unroll 4
   for (int item = tid; item < n_items; item += S::NTHR) {
@@ -1357,18 +1361,16 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
     float M = NEG_INF;
 #pragma unroll
     for (int r = 0; r < S::NRG; ++r)
-      M = fmaxf(M, stat[(((S::RSPLIT ? 2 : 1) * (r * S::HG + hgi)) * 16 + nn) * 2]);
+      M = fmaxf(M, stat[((r * S::HG + hgi) * 16 + nn) * 2]);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float L = 0.f;
     if (M != NEG_INF) {
 #pragma unroll
       for (int r = 0; r < S::NRG; ++r) {
         const int w = r * S::HG + hgi;
-        // PAIR: waves w, w+1 hold one head's row halves; RSPLIT: slots 2w, 2w+1
-        const int sw = S::RSPLIT ? 2 * w : w;
-        const float fct = fast_exp2(stat[(sw * 16 + nn) * 2] - M);
-        L += fct * (stat[(sw * 16 + nn) * 2 + 1] +
-                    ((S::PAIR || S::RSPLIT) ? stat[((sw + 1) * 16 + nn) * 2 + 1] : 0.f));
+        // PAIR: waves w, w + 1 hold one head's row halves
+        const float fct = fast_exp2(stat[(w * 16 + nn) * 2] - M);
+        L += fct * (stat[(w * 16 + nn) * 2 + 1] + (S::PAIR ? stat[((w + 1) * 16 + nn) * 2 + 1] : 0.f));
         // dims 8c..8c+7 = fragment c/2, lanes (2*(c&1) + {0,1})*16 + nn, j = 0..3
         const f32x4* ost = reinterpret_cast<const f32x4*>(smem) + (size_t)w * 32 * 64 + (c >> 1) * 64;
         const f32x4 v0 = ost[(2 * (c & 1) + 0) * 16 + nn];
@@ -1389,10 +1391,8 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
       for (int j = 0; j < 4; ++j)
         pk[j] = (uint32_t)f32_to_bf16_bits(acc[2 * j] * inv) |
                 ((uint32_t)f32_to_bf16_bits(acc[2 * j + 1] * inv) << 16);
-      const int orow = S::DENSE ? d_r0 + head / a.h : t;
-      const int ohead = S::DENSE ? head - (head / a.h) * a.h : head;
-      *reinterpret_cast<u32x4*>(a.out + (int64_t)orow * a.out_st + (int64_t)ohead * a.out_sh + 8 * c) = pk;
-      if (c == 0) a.lse[(int64_t)orow * a.lse_st + ohead] = lse_v;
+      *reinterpret_cast<u32x4*>(a.out + (int64_t)t * a.out_st + (int64_t)head * a.out_sh + 8 * c) = pk;
+      if (c == 0) a.lse[(int64_t)t * a.lse_st + head] = lse_v;
     } else {
       float* wo = a.ws_out + ((unit * a.h + head) * D_V) + 8 * c;
       f32x4 w0, w1;
