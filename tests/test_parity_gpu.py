@@ -451,6 +451,19 @@ def test_c5_fp8_two_per_cu_sampled():
     check(out[rows], lse[rows], *oracle(c, rows=rows), what="c5 two-per-CU")
 
 
+@pytest.mark.parametrize("h,kv_format", [(8, "bf16"), (32, "bf16"), (16, "fp8")])
+def test_two_per_cu_shapes_deterministic(h, kv_format):
+    """Repeated calls of the two-per-CU shapes give the same bits, split and
+    unsplit (two work-groups sharing a CU never share LDS or outputs)."""
+    say("two-per-CU determinism", h, kv_format)
+    c = G.make_mini(seed=45, num_heads=h, topk=300, kv_format=kv_format, num_seqs=12, tokens_per_seq=48)
+    dev = Dev(c)
+    for splits in (1, 3):
+        a = to_np(*run_gpu(dev, variant=2, num_splits=splits))
+        b = to_np(*run_gpu(dev, variant=2, num_splits=splits))
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
 def test_c2_decode_two_per_cu_shape():
     say("c2 two-per-CU")
     c = G.make_config("c2_decode")
