@@ -1,21 +1,27 @@
 #!/usr/bin/env python3
 """Benchmark of the sparse MLA forward (top-k = 2048) on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload c2_decode]
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
 
 A step is one sparse_mla_fwd call over one synthetic batch (index
 compaction + gather + QK^T + softmax + PV + split merge when the plan splits).
 Inputs are resident in HBM before timing starts.  K steps are timed with HIP
 events on the stream the library launches on, bracketed by device syncs.
-Prints ONE JSON line: throughput in query-tokens/s, the dominant kernel's
-roofline (per-launch durations from events around each launch), the same
-step replayed from a HIP graph (checked bit for bit against the eager
-result), the kernel after evicting the caches (1 GiB read between launches),
-and the CPU oracle timed on a bounded sample of the same workload on this
-host.
+Prints ONE JSON line.
 
-Workloads (synthetic, seeded; `--workload`):
-  c2_decode (default)  32 rows x 1 query, h=8, 16384-token contexts
+Default run: the headline line is the largest single-GPU workload, c5_fp8
+(32768 query rows, h=8, fp8 latent cache, top-k 2048): throughput in
+query-tokens/s, the attention kernel's roofline (per-launch durations from
+HIP events around each launch, HBM-bound), the kernel after evicting the
+caches, and the CPU oracle (fp32) timed on a bounded sample of the same
+workload on this host.  The same line carries two more measured workloads
+under their own keys, each with its own roofline: "c4_long_prefill"
+(16384 rows, h=64, bf16: the MFMA-bound target) and "c2_decode" (32 rows,
+h=8, split-KV + merge, also replayed from a HIP graph).
+
+Workloads (synthetic, seeded; `--workload` runs one of them alone):
+  c5_fp8               32768 rows over 16 sequences (histories 8192..131072), h=8, fp8 cache
+  c2_decode            32 rows x 1 query, h=8, 16384-token contexts
   c1_tiny              64 rows, h=8, topk=128
   c3_h{8,16,32,64}     4096 rows over 8 x (8192 + 512) tokens; suffix _pad64 for the padded tiling,
                        _nope for the NoPE geometry (512-wide rows, no rope part)
@@ -46,15 +52,16 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="c2_decode")
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="headline",
+                    help="headline (c5_fp8 line + c4_long_prefill and c2_decode keys) or one workload")
     ap.add_argument("--splits", type=int, default=0, help="0 = automatic plan")
     ap.add_argument("--variant", type=int, default=0)
     ap.add_argument("--gather-order", default="auto", choices=["auto", "list", "slot"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--cold-launches", type=int, default=50)
+    ap.add_argument("--cold-launches", type=int, default=10)
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--copy-reference", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (calibrates HBM byte counters)")
@@ -116,8 +123,20 @@ def counted_traffic(workload_name):
     return None, None
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(case, seconds):
-    """The oracle, as it stands, on a bounded sample of the workload's rows."""
+    """The oracle, as it stands, in fp32 on a bounded sample of the
+    workload's rows (random order, cycling), on this host's cores."""
     from oracle import sparse_mla_oracle as O
     try:
         import threadpoolctl
@@ -128,7 +147,7 @@ def cpu_baseline(case, seconds):
     rng = np.random.default_rng(0)
     order = rng.permutation(T)
     kw = dict(topk=case.topk, scale=case.scale, kv_format=case.kv_format, page_size=case.page_size,
-              index_mode="logical", block_table=case.block_table, token_seq=case.token_seq)
+              index_mode="logical", block_table=case.block_table, token_seq=case.token_seq, dtype=np.float32)
     done = 0
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < seconds:
@@ -136,9 +155,10 @@ def cpu_baseline(case, seconds):
         O.sparse_mla_forward(case.q, case.kv, case.topk_idx, rows=rows, **kw)
         done += len(rows)
     el = time.perf_counter() - t0
-    return {"value": done / el, "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": "%d query rows (random order, cycling over all %d rows of the workload) in %.1f s, "
-                      "numpy fp64 oracle" % (done, T, el)}
+    return {"value": round(done / el, 2), "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "sample": "%d query rows of %s (random order over all %d rows) in %.1f s; numpy oracle in fp32 "
+                      "(per-row Python gather, BLAS with %d threads)" % (done, case.name, T, el, threads)}
 
 
 def bench_topk(args):
@@ -176,28 +196,18 @@ def bench_topk(args):
     print(json.dumps(res), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs the sparse MLA forward on a single "
-              "MI355X (no collectives); --gpus %d is not supported." % args.gpus, flush=True)
-        sys.exit(2)
+def run_workload(args, name, *, graph, cold_launches):
+    """Time one workload: K steps (value), per-launch kernel durations
+    (roofline), optional HIP-graph replay (checked bit for bit) and cold-cache
+    launches.  Returns (result dict, case)."""
     import torch
-    if args.copy_reference:
-        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_reference_bytes_read": src.numel() * 4, "launches": 5}), flush=True)
-        return
     from sparse_mla_attention_04_amd import binding as B
     from sparse_mla_attention_04_amd.inputs import DeviceCase as Dev
 
-    if args.workload == "topk_4096x65536":
-        return bench_topk(args)
-    case, tiling, wl_name = workload(args.workload)
+    t_gen = time.perf_counter()
+    case, tiling, wl_name = workload(name)
     dev = Dev(case)
+    t_gen = time.perf_counter() - t_gen
     T, h = case.num_tokens, case.num_heads
     q = dev.q[:, :h, :]
     out = torch.empty((T, h, 512), dtype=torch.bfloat16, device="cuda")
@@ -247,7 +257,8 @@ def main():
     wall = time.perf_counter() - w0
     ms_per_step = e0.elapsed_time(e1) / args.steps
 
-    # ---- dominant kernel: per-launch durations (events around each launch)
+    # ---- dominant kernel: per-launch durations (events around each launch,
+    #      on torch's current stream, which is the stream the library launches on)
     K2 = max(20, min(args.steps, 500))
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K2)]
     for a, b in evs:
@@ -260,8 +271,8 @@ def main():
 
     # ---- the same step replayed from a HIP graph (launch overhead of the
     #      serving setting); every replay must reproduce the eager result bit for bit
-    graph = None
-    if not args.no_graph:
+    graph_res = None
+    if graph and not args.no_graph:
         step()
         torch.cuda.synchronize()
         ref_out, ref_lse = out.clone(), lse.clone()
@@ -294,24 +305,24 @@ def main():
         g1.record()
         torch.cuda.synchronize()
         gms = g0.elapsed_time(g1) / args.steps
-        graph = {"ms_per_step": round(gms, 6), "query_tokens_per_s": round(T / (gms * 1e-3), 1),
-                 "replays_checked_bitwise": checked}
+        graph_res = {"ms_per_step": round(gms, 6), "query_tokens_per_s": round(T / (gms * 1e-3), 1),
+                     "replays_checked_bitwise": checked}
         del g
 
     # ---- same kernel after evicting caches (1 GiB read between launches, not timed;
     #      reading leaves no dirty lines behind that the kernel would have to write back)
-    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     cold = []
-    for _ in range(args.cold_launches):
-        flush.sum()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        kernel_only()
-        b.record()
-        torch.cuda.synchronize()
-        cold.append(a.elapsed_time(b))
-    cold_ms = float(np.median(cold))
-    del flush
+    if cold_launches > 0:
+        flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        for _ in range(cold_launches):
+            flush.sum()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            kernel_only()
+            b.record()
+            torch.cuda.synchronize()
+            cold.append(a.elapsed_time(b))
+        del flush
 
     # dense: every row attends to its whole prefix (positions + 1 cache rows)
     n_valid = int((case.positions.astype(np.int64) + 1).sum()) if dense else algorithmic_counts(case)
@@ -320,59 +331,129 @@ def main():
     gathered = n_valid * row_bytes
     flops = n_valid * h * 2 * (d_qk + 512)
     tokens_per_s = T / (ms_per_step * 1e-3)
+    traffic, traffic_note = counted_traffic(name)
     hbm_bound = h < 64 and not dense
     if hbm_bound:
         achieved = gathered / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
+        if achieved > HBM_PEAK_GBPS:
+            # the pool is served from L2 / MALL across query rows: the gathered-byte rate
+            # is an effective (cache-served) rate, not an HBM fraction
+            roof["effective_cache_served"] = True
+            roof["frac"] = None
+            roof["frac_counted_hbm"] = (round(traffic / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+                                        if traffic is not None else None)
+            roof["mfma_frac_real_heads"] = round(flops / (kern_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
     else:
         achieved = flops / (kern_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
-    traffic, traffic_note = counted_traffic(args.workload)
     roof["traffic"] = None if traffic is None else round(traffic)
     roof["traffic_note"] = traffic_note
     roof["kernel"] = "smla_fwd" + (" (dense causal)" if dense else "" if pl.num_splits == 1 else " (split partials)")
     roof["kernel_us"] = round(kern_ms * 1e3, 2)
-    roof["kernel_us_p10_p50_p90"] = [round(float(np.percentile(kern_all, q)) * 1e3, 2) for q in (10, 50, 90)]
+    roof["kernel_us_p10_p50_p90"] = [round(float(np.percentile(kern_all, q_)) * 1e3, 2) for q_ in (10, 50, 90)]
+    roof["launches_timed"] = K2
     roof["algorithmic_bytes"] = gathered
     roof["algorithmic_flops"] = flops
+    roof["per_unit"] = ("one valid gathered row: %d B, %d flop (2 x h x (%d + 512))"
+                        % (row_bytes, h * 2 * (d_qk + 512), d_qk))
 
+    config = ({"workload": wl_name, "entry": "sparse_mla_fwd",
+               "num_tokens": T, "num_heads": h, "topk": case.topk,
+               "kv_format": case.kv_format, "page_size": case.page_size, "tiling": tiling,
+               "num_splits": pl.num_splits, "kernel_variant": pl.kernel_variant,
+               "gather_order": {1: "list", 2: "slot"}[pl.gather_order],
+               "grid": pl.grid, "threads": pl.threads} if not dense else
+              {"workload": wl_name, "entry": "sparse_mla_dense_fwd", "num_tokens": T, "num_heads": h,
+               "kv_format": case.kv_format, "page_size": case.page_size,
+               "rows_per_work_group": 64 // h, "kernel": "pipelined h=64 schedule, (row, head) query slots",
+               "grid": ((T + 64 // h - 1) // (64 // h) + case.block_table.shape[0] + 7) // 8 * 8, "threads": 256})
+    res = {
+        "value": round(tokens_per_s, 1),
+        "unit": "query-tokens/s",
+        "ms_per_step": round(ms_per_step, 6),
+        "steps": args.steps,
+        "dtype": "fp8_e4m3+bf16" if case.kv_format == "fp8" else "bf16",
+        "config": config,
+        "gathered_GBps_per_step": round(gathered / (ms_per_step * 1e-3) / 1e9, 1),
+        "mfma_frac_per_step": round(flops / (ms_per_step * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 5),
+        "wall_s_timed": round(wall, 4),
+        "input_generation_s": round(t_gen, 1),
+        "roofline": roof,
+        "graph": graph_res,
+    }
+    if cold:
+        cold_ms = float(np.median(cold))
+        res["cold_cache"] = {"kernel_us_median": round(cold_ms * 1e3, 2), "launches": len(cold),
+                             "gathered_GBps": round(gathered / (cold_ms * 1e-3) / 1e9, 1),
+                             "hbm_frac": round(gathered / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                             "note": "1 GiB read between launches to evict L2 and MALL"}
+    del out, lse, ws, pws, dev, q
+    torch.cuda.empty_cache()
+    return res, case
+
+
+DTYPE_NOTE = {"fp8_e4m3+bf16": "fp8 e4m3 latent cache dequantised exactly to bf16; bf16 MFMA with fp32 "
+                               "accumulation and fp32 softmax",
+              "bf16": "bf16 cache and MFMA with fp32 accumulation and fp32 softmax"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the sparse MLA forward on a single "
+              "MI355X (no collectives); --gpus %d is not supported." % args.gpus, flush=True)
+        sys.exit(2)
+    import torch
+    if args.copy_reference:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_reference_bytes_read": src.numel() * 4, "launches": 5}), flush=True)
+        return
+    if args.workload == "topk_4096x65536":
+        return bench_topk(args)
+
+    headline = args.workload == "headline"
+    main_name = "c5_fp8" if headline else args.workload
+    print("bench: %s" % main_name, file=sys.stderr, flush=True)
+    res_main, case_main = run_workload(args, main_name, graph=not headline and main_name == "c2_decode",
+                                       cold_launches=args.cold_launches)
+    extras = {}
+    if headline:
+        for name, graph in (("c4_long_prefill", False), ("c2_decode", True)):
+            print("bench: %s" % name, file=sys.stderr, flush=True)
+            r, _ = run_workload(args, name, graph=graph, cold_launches=args.cold_launches)
+            r.pop("steps", None)
+            extras[name] = r
     res = {
         "metric": METRIC,
-        "value": round(tokens_per_s, 1),
+        "value": res_main["value"],
         "unit": "query-tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 6),
+        "ms_per_step": res_main["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": wl_name, "entry": "sparse_mla_dense_fwd" if dense else "sparse_mla_fwd",
-                   "num_tokens": T, "num_heads": h, "topk": case.topk,
-                   "kv_format": case.kv_format, "page_size": case.page_size, "tiling": tiling,
-                   "num_splits": pl.num_splits, "kernel_variant": pl.kernel_variant,
-                   "gather_order": {1: "list", 2: "slot"}[pl.gather_order],
-                   "grid": pl.grid, "threads": pl.threads} if not dense else
-                  {"workload": wl_name, "entry": "sparse_mla_dense_fwd", "num_tokens": T, "num_heads": h,
-                   "kv_format": case.kv_format, "page_size": case.page_size,
-                   "rows_per_work_group": 64 // h, "kernel": "pipelined h=64 schedule, (row, head) query slots",
-                   "grid": ((T + 64 // h - 1) // (64 // h) + case.block_table.shape[0] + 7) // 8 * 8, "threads": 256},
-        "gathered_GBps_per_step": round(gathered / (ms_per_step * 1e-3) / 1e9, 1),
-        "mfma_frac_per_step": round(flops / (ms_per_step * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 5),
-        "wall_s_timed": round(wall, 4),
-        "roofline": roof,
-        "graph": graph,
-        "cold_cache": {"kernel_us_median": round(cold_ms * 1e3, 2),
-                       "gathered_GBps": round(gathered / (cold_ms * 1e-3) / 1e9, 1),
-                       "hbm_frac": round(gathered / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                       "note": "1 GiB read between launches to evict L2 and MALL"},
+        "dtype": res_main["dtype"],
+        "dtype_note": DTYPE_NOTE[res_main["dtype"]],
+        "data": "synthetic (seeded; shapes and distributions of the workload, no dataset)",
+        "config": res_main["config"],
     }
+    for k in ("gathered_GBps_per_step", "mfma_frac_per_step", "wall_s_timed", "input_generation_s", "roofline",
+              "graph", "cold_cache"):
+        if k in res_main:
+            res[k] = res_main[k]
+    res.update(extras)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+        print("bench: cpu baseline", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(case_main, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

@@ -2,8 +2,19 @@
 HIP path through the C ABI, run the CPU oracle on the same host arrays, and
 compare with the stated tolerances.
 
-Tolerances (floating point): out |err| <= 1e-2 + 1e-2 * |ref| (bf16 output),
-lse |err| <= 1e-3, split vs unsplit within 1e-3; -inf must match -inf.
+Tolerances (floating point):
+  * against the oracle: out |err| <= 1e-2 + 1e-2 * |ref| (bf16 output),
+    lse |err| <= 1e-3; -inf must match -inf;
+  * split vs unsplit (and any two kernel paths that differ only in the
+    order of fp32 sums or in the exponent reference their bf16 P is formed
+    with): the fp32 results agree within 1e-3 -- compared on the fp32
+    partials the kernel writes before any bf16 rounding, the unsplit row
+    (one partial) against the split partials merged by the oracle's
+    lse_combine in fp64;
+  * the same pair compared after the final bf16 rounding: each side is the
+    round-to-nearest-even of an fp32 value, so two values within 1e-3 round
+    to results within 1e-3 + one bf16 ulp of the larger magnitude
+    (|rne(x) - rne(y)| <= |x - y| + ulp/2 + ulp/2).
 """
 from __future__ import annotations
 
@@ -62,6 +73,99 @@ def run_gpu(dev: Dev, *, heads=None, logical=True, idx_t=None, tiling="auto", nu
     B.fwd(q, dev.kv, idx, out, lse, topk=p.topk, scale=c.scale, workspace=workspace,
           block_table=dev.bt if logical else None, token_seq=dev.ts if logical else None, params=p)
     return out, lse
+
+
+def run_partials(dev: Dev, *, num_splits, heads=None, logical=True, idx_t=None, tiling="auto", variant=0,
+                 topk=None, gather_order="auto"):
+    """sparse_mla_fwd_partials through the binding with a forced split count.
+    Returns host fp32 (out [T, S, h, 512], lse [T, S, h]): unit t * S + s."""
+    c = dev.case
+    h = c.num_heads if heads is None else heads
+    q = dev.q[:, :h, :]
+    T, S = c.num_tokens, int(num_splits)
+    idx = dev.idx if idx_t is None else idx_t
+    dummy_out = torch.empty((0, h, 512), dtype=torch.bfloat16)
+    dummy_lse = torch.empty((0, h), dtype=torch.float32)
+    p = B.params_for(q, dev.kv, idx, dummy_out, dummy_lse, topk=c.topk if topk is None else topk, scale=c.scale,
+                     page_size=c.page_size, kv_format=c.kv_format,
+                     block_table=dev.bt if logical else None, token_seq=dev.ts if logical else None,
+                     tiling=tiling, num_splits=S, kernel_variant=variant, gather_order=gather_order)
+    p.num_tokens = T
+    p.out_stride_t, p.out_stride_h, p.lse_stride_t = h * 512, 512, h
+    U = T * S
+    ws = torch.empty(U * h * 513 * 4 + 16, dtype=torch.uint8, device=dev.q.device)
+    B.fwd_partials(q, dev.kv, idx, ws, topk=p.topk, scale=c.scale, block_table=dev.bt if logical else None,
+                   token_seq=dev.ts if logical else None, params=p)
+    torch.cuda.synchronize()
+    f = ws[:U * h * 513 * 4].view(torch.float32)
+    po = f[:U * h * 512].view(T, S, h, 512).cpu().numpy()
+    pl = f[U * h * 512:].view(T, S, h).cpu().numpy()
+    return po, pl
+
+
+def merge_partials(po, pl):
+    """The oracle's lse_combine applied row by row (fp64): [T, S, h, 512],
+    [T, S, h] -> out [T, h, 512], lse [T, h]."""
+    T = po.shape[0]
+    out = np.zeros((T,) + po.shape[2:], dtype=np.float64)
+    lse = np.zeros((T, po.shape[2]), dtype=np.float64)
+    for t in range(T):
+        out[t], lse[t] = O.lse_combine(po[t], pl[t])
+    return out, lse
+
+
+def check_fp32_pair(out_a, lse_a, out_b, lse_b, what="", atol=SPLIT_ATOL):
+    """Two fp32 results of the same rows within `atol` element by element
+    (out and lse); -inf patterns equal.  Returns the largest differences."""
+    out_a, out_b = np.asarray(out_a, np.float64), np.asarray(out_b, np.float64)
+    lse_a, lse_b = np.asarray(lse_a, np.float64), np.asarray(lse_b, np.float64)
+    assert out_a.shape == out_b.shape and lse_a.shape == lse_b.shape
+    assert np.array_equal(np.isneginf(lse_a), np.isneginf(lse_b)), what + ": -inf lse pattern differs"
+    do = float(np.abs(out_a - out_b).max()) if out_a.size else 0.0
+    fin = np.isfinite(lse_a)
+    dl = float(np.abs(lse_a[fin] - lse_b[fin]).max()) if fin.any() else 0.0
+    say("  %s: fp32 out diff %.3g, lse diff %.3g" % (what, do, dl))
+    assert do <= atol, "%s: fp32 out differs by %.4g > %g" % (what, do, atol)
+    assert dl <= atol, "%s: lse differs by %.4g > %g" % (what, dl, atol)
+    return do, dl
+
+
+def bf16_ulp(x):
+    """Spacing of bf16 numbers at |x| (8 significand bits; subnormals ignored)."""
+    ax = np.maximum(np.abs(np.asarray(x, np.float64)), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(ax)) - 7)
+
+
+def check_bf16_pair(out_a, out_b, what="", atol=SPLIT_ATOL):
+    """Two bf16 outputs whose fp32 sources agree within `atol`: element-wise
+    |a - b| <= atol + one bf16 ulp of max(|a|, |b|)."""
+    a, b = np.asarray(out_a, np.float64), np.asarray(out_b, np.float64)
+    bound = atol + bf16_ulp(np.maximum(np.abs(a), np.abs(b)))
+    err = np.abs(a - b)
+    bad = err > bound
+    assert not bad.any(), "%s: %d bf16 outputs differ beyond 1e-3 + 1 ulp; worst %.4g at %s" % (
+        what, int(bad.sum()), err.max(), np.unravel_index(err.argmax(), err.shape))
+
+
+def stratified_rows(case, n=2048, seed=0):
+    """At least n query rows spread over the whole batch: every sequence's
+    first and last row, n - that many evenly spaced rows (covering every
+    XCD's contiguous share of work units), each shifted by a seeded random
+    offset inside its stride."""
+    T = case.num_tokens
+    if T <= n:
+        return list(range(T))
+    rows = set()
+    for s in np.unique(case.token_seq):
+        r = np.nonzero(case.token_seq == s)[0]
+        rows.add(int(r[0]))
+        rows.add(int(r[-1]))
+    rng = np.random.default_rng(seed)
+    stride = T / n
+    base = np.floor(np.arange(n) * stride).astype(np.int64)
+    off = rng.integers(0, max(1, int(stride)), size=n)
+    rows.update(int(x) for x in np.minimum(base + off, T - 1))
+    return sorted(rows)
 
 
 def to_np(out, lse):
