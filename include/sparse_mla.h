@@ -24,15 +24,17 @@
  *     row, stored in buffers wider than top-k (2051 columns).
  *   - vLLM PR #64510, section "Details": the real head count (8/16/32) is
  *     run natively instead of padding heads to 64.
- *   - prhub report on vLLM PR #55738, "Details" items 1 and 3: a NoPE MLA
- *     layout has a zero-width rope part (qk_rope 0), and K is then the
- *     latent part alone (SMLA_GEOM_NOPE below).
+ *   - prhub report on vLLM PR #55738, "Implementation breakdown" items 1
+ *     and 3: a NoPE MLA layout has a zero-width rope part (qk_rope 0), and K
+ *     is then the latent part alone (SMLA_GEOM_NOPE below); item 5: with a
+ *     quantised cache such layers stay on the per-token top-k MQA path.
  *
  * Conventions fixed by this ABI (the pages leave them open):
  *   - A cache row is 576 values: dims 0..511 latent, 512..575 rope.  The
  *     value vector of a row is its first 512 dims.  With geometry
  *     SMLA_GEOM_NOPE rows and query heads are the 512 latent dims alone
- *     (bf16 cache only: row `slot` at byte slot * 1024).
+ *     (bf16 cache: row `slot` at byte slot * 1024; fp8 cache: rows of the
+ *     512 codes alone, see below).
  *   - The cache is paged; page_size rows per page (a power of two; 64 in
  *     the configurations this library is tuned for).
  *       bf16 cache: row `slot` lives at byte slot * 1152.
@@ -41,6 +43,9 @@
  *         [512 OCP E4M3FN codes | 64 bf16 rope values], followed by
  *         page_size x 4 fp32 scales (one per 128 latent dims).  The latent
  *         value of dim d is e4m3(code[d]) * scale[d / 128]; rope is bf16.
+ *         SMLA_GEOM_NOPE: page p starts at byte p * page_size * 528 and
+ *         holds page_size rows of the 512 codes, then the page_size x 4
+ *         scales.
  *   - Index entries equal to -1 are skipped.  Any entry that is negative,
  *     or whose physical row falls outside [0, num_pages * page_size) (or,
  *     in LOGICAL mode, whose block lies outside the block table, or whose
@@ -98,8 +103,8 @@ extern "C" {
 
 /* geometry (smla_params.geometry): the width of query heads and cache rows.
  * MLA: 576 = 512 latent + 64 rope dims.  NOPE: 512 latent dims, no rope
- * part (bf16 caches, kernel_variant 0, or 2 at h <= 32; anything else ->
- * SMLA_ERR_UNSUPPORTED).
+ * part (bf16 caches: kernel_variant 0, or 2 at h <= 32; fp8 caches:
+ * kernel_variant 0, or 2 at h <= 16; anything else -> SMLA_ERR_UNSUPPORTED).
  * The output is 512 wide either way.  0 is MLA, so zero-initialised params
  * keep the rope part. */
 #define SMLA_GEOM_MLA 0
@@ -177,7 +182,11 @@ typedef struct smla_plan {
                                /* bf16 or h <= 16 fp8, else 0)                       */
 } smla_plan;
 
-/* Bytes of workspace sparse_mla_fwd needs for calls described by *p.
+/* Bytes of workspace sparse_mla_fwd needs for calls described by *p: the
+ * fp32 split-KV partials that vLLM PR #60220 ("Limitations"; "Details",
+ * root cause) reports a kernel allocating on every call, outside the startup
+ * memory profile (2 x T x 64 x 512 x 4 B = 8 GiB at T = 32K), held here in a
+ * caller buffer sized once.
  * Host-only, pure and independent of the device.  For num_splits == 0 the
  * result does not depend on num_tokens (it covers every automatic plan:
  * SMLA_MAX_SPLIT_UNITS * h * 513 * 4 bytes), so a caller can size the

@@ -23,9 +23,11 @@ query row t:
      exactly; fp8 rows are code value x block scale for the latent part (one
      fp32 scale per 128 dims) and bf16 for the rope part.  In the NoPE
      geometry the rope part has zero width and rows are the 512 latent dims
-     (prhub report on vLLM PR #55738, "Details" items 1 and 3: qk_rope 0, and
-     the K concat with an empty rope part is the latent part itself); the
-     width is taken from q (bf16 caches only).
+     (prhub report on vLLM PR #55738, "Implementation breakdown" items 1
+     and 3: qk_rope 0, and the K concat with an empty rope part is the
+     latent part itself); the width is taken from q.  An fp8 NoPE row is the
+     512 scaled codes alone (the same report's item 5: quantised-KV prefill
+     stays on the per-token top-k MQA path).
   4. All h heads of the row share the gathered rows (MQA / absorbed form,
      prhub report on PR #55738, "Motivation": the per-token top-k MQA
      kernel).  Scores S = (Q @ R^T) * scale.
@@ -46,7 +48,6 @@ import numpy as np
 D_LATENT = 512
 D_ROPE = 64
 D_QK = 576
-FP8_ROW = 640          # bytes of [512 codes | 64 bf16 rope]
 FP8_SCALES = 16        # bytes of the four fp32 block scales
 
 
@@ -102,14 +103,16 @@ def translate(j: int, index_mode: str, page_size: int, num_slots: int,
     return int(slot)
 
 
-def fp8_rows(kv_pages: np.ndarray, slots: np.ndarray, page_size: int):
+def fp8_rows(kv_pages: np.ndarray, slots: np.ndarray, page_size: int, rope_dims: int = D_ROPE):
     """Read fp8 cache rows from the paged byte layout: page p holds P rows of
-    [512 code bytes | 64 bf16 rope] followed by P x 4 fp32 scales.
-    Returns codes uint8 [n, 512], scales fp32 [n, 4], rope bf16 bits [n, 64]."""
+    [512 code bytes | rope_dims bf16 rope values] followed by P x 4 fp32
+    scales (rope_dims is 64, or 0 in the NoPE geometry).
+    Returns codes uint8 [n, 512], scales fp32 [n, 4], rope bf16 bits [n, rope_dims]."""
     slots = np.asarray(slots, dtype=np.int64)
     npages = kv_pages.shape[0]
-    body = kv_pages[:, :page_size * FP8_ROW].reshape(npages, page_size, FP8_ROW)
-    tail = kv_pages[:, page_size * FP8_ROW:page_size * (FP8_ROW + FP8_SCALES)].reshape(
+    row = D_LATENT + 2 * rope_dims
+    body = kv_pages[:, :page_size * row].reshape(npages, page_size, row)
+    tail = kv_pages[:, page_size * row:page_size * (row + FP8_SCALES)].reshape(
         npages, page_size, FP8_SCALES)
     page, r = slots // page_size, slots % page_size
     rows = body[page, r]
@@ -125,8 +128,8 @@ def gather_rows(kv: np.ndarray, slots, kv_format: str, page_size: int, dtype=np.
     512 in the NoPE geometry)."""
     slots = np.asarray(slots, dtype=np.int64)
     n = slots.shape[0]
-    if d_qk not in (D_QK, D_LATENT) or (d_qk != D_QK and kv_format != "bf16"):
-        raise ValueError("row width %d with %s cache" % (d_qk, kv_format))
+    if d_qk not in (D_QK, D_LATENT):
+        raise ValueError("row width %d" % d_qk)
     R = np.zeros((n, d_qk), dtype=dtype)
     if n == 0:
         return R
@@ -134,11 +137,12 @@ def gather_rows(kv: np.ndarray, slots, kv_format: str, page_size: int, dtype=np.
         flat = kv.reshape(-1, d_qk)
         R[:] = bf16_to_float(flat[slots], dtype)
     elif kv_format == "fp8":
-        codes, scales, rope = fp8_rows(kv, slots, page_size)
+        codes, scales, rope = fp8_rows(kv, slots, page_size, rope_dims=d_qk - D_LATENT)
         vals = E4M3FN_TABLE[codes]                                   # exact code values
         blk_scale = np.repeat(scales.astype(np.float64), 128, axis=1)  # scale of dim d = scales[d // 128]
         R[:, :D_LATENT] = (vals * blk_scale).astype(dtype)
-        R[:, D_LATENT:] = bf16_to_float(rope, dtype)
+        if d_qk > D_LATENT:
+            R[:, D_LATENT:] = bf16_to_float(rope, dtype)
     else:
         raise ValueError(kv_format)
     return R
@@ -178,7 +182,8 @@ def sparse_mla_forward(q: np.ndarray, kv: np.ndarray, topk_idx: np.ndarray, *, t
                        num_heads=None, rows=None, dtype=np.float64):
     """The whole definition.  q: uint16 bf16 bits [T, H, 576] ([T, H, 512]
     for the NoPE geometry); kv: the paged cache (bf16 bits [pages, P, d] with
-    the same d, or fp8 bytes [pages, page_bytes]);
+    the same d, or fp8 bytes [pages, page_bytes], rows with or without the
+    rope part following q's width);
     topk_idx: int32 [T, >= topk].  Returns (out [n, h, 512], lse [n, h]) for
     the requested rows (all rows by default)."""
     T = q.shape[0]

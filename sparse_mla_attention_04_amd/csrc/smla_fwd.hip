@@ -53,7 +53,8 @@ constexpr int D_V = 512;
 constexpr int ROW_BYTES = D_QK * 2;     // bf16 cache row
 constexpr int NOPE_ROW_BYTES = D_V * 2; // bf16 cache row of the NoPE geometry (no rope part)
 constexpr int FP8_ROW_BYTES = 640;      // fp8 cache row: 512 code bytes + 64 bf16 rope
-constexpr int FP8_SLOT_BYTES = 656;     // per-row share of an fp8 page (row + four fp32 scales)
+constexpr int FP8_NOPE_ROW_BYTES = 512; // fp8 cache row of the NoPE geometry: the 512 code bytes
+constexpr int FP8_SCALE_BYTES = 16;     // four fp32 block scales per fp8 row, after the page's rows
 constexpr int LIST_CAP = kListCap;      // index entries compacted per pass
 constexpr float NEG_INF = -__builtin_inff();
 constexpr float LN2 = 0.69314718055994530942f;
@@ -74,7 +75,8 @@ struct Shape {
   static constexpr int RH_PER_WAVE = NRH / HG;
   // NOPE: the NoPE geometry, rows and queries of the 512 latent dims only
   static constexpr bool NOPE = NOPE_;
-  static constexpr int ROWB = FP8 ? FP8_ROW_BYTES : NOPE ? NOPE_ROW_BYTES : ROW_BYTES;  // bytes per cache row
+  static constexpr int ROWB = FP8 ? (NOPE ? FP8_NOPE_ROW_BYTES : FP8_ROW_BYTES)
+                                 : NOPE ? NOPE_ROW_BYTES : ROW_BYTES;  // bytes per cache row
   static constexpr int KS = NOPE ? 16 : 18;           // 32-dim k-steps of a score
   static constexpr int NLINES = ROWB / 128;           // 128-B lines per row
   static constexpr int BODY_BYTES = RT * NLINES * 128;
@@ -129,13 +131,14 @@ struct Shape {
   static_assert(!FP8 || RT == 32, "the fp8 P.V step pairs two 16-row fragments");
   static_assert(NRH % HG == 0, "DMA groups must split evenly over the waves of a row group");
   static_assert((NST - 1) * PER <= 63, "vmcnt holds at most 63 outstanding loads");
-  static_assert(NW * 32 * 64 * 16 <= STAT_OFF, "epilogue staging must fit below the statistics");
+  // epilogue staging: every wave's 32 accumulator fragments (a wave pair
+  // stages its row stream's 32 fragments once)
+  static_assert((PAIR_ ? NRG : NW) * 32 * 64 * 16 <= STAT_OFF, "epilogue staging must fit below the statistics");
   static_assert(NW * 8 * 4 <= 512, "compaction counts");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(LIST_CAP % NTHR == 0, "compaction split");
   static_assert(!DSPLIT || (HG == 4 && NRG == 1 && RT == 32 && !FP8), "output-dim split layout");
   static_assert(!PIPE || (DSPLIT && NST >= 3 && PER == NLINES), "pipelined variant layout");
-  static_assert(!NOPE || !FP8, "the NoPE geometry is built for bf16 caches");
   // DENSE (with PIPE): dense causal mode.  A work-group takes a block of up to
   // 64 / h consecutive query rows of one sequence; its 64 query slots are
   // (row, head) pairs m = row * h + head, and every cache row of positions
@@ -194,6 +197,14 @@ __device__ __forceinline__ float wave_xor(float v, int m) { return __shfl_xor(v,
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Exponent reference of a head: a base-2 score maximum rounded up to an
+// integer.  With integer references P = 2^(x - m) is, for any m, the same
+// bf16 value up to an exact power of two, so a row split into KV chunks
+// (each with its own reference) rounds every P exactly as the unsplit row
+// does, and the lse-weighted merge of the chunks reproduces the unsplit
+// result up to fp32 summation order.  -inf (no score yet) stays -inf.
+__device__ __forceinline__ float int_ref(float m) { return __builtin_ceilf(m); }
+
 // max over lanes l, l^16, l^32, l^48 with the gfx950 lane-swap instructions
 // (rows of 16 lanes swapped, then halves of 32), no LDS traffic
 __device__ __forceinline__ float max_xor16_32(float v) {
@@ -209,13 +220,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
 }
 
 // Byte offset of a cache row: bf16 rows are contiguous; fp8 pages hold the
-// page's rows first ([512 codes | 64 bf16 rope] each) and then their scales.
+// page's rows first ([512 codes | 64 bf16 rope] each, or the 512 codes alone
+// in the NoPE geometry) and then their scales.
 template <bool FP8, int ROWB>
 __device__ __forceinline__ int64_t row_offset(const FwdArgs& a, int slot) {
   if constexpr (FP8) {
     const int64_t page = slot >> a.page_shift;
     const int64_t rin = slot & ((1 << a.page_shift) - 1);
-    return page * ((int64_t)FP8_SLOT_BYTES << a.page_shift) + rin * FP8_ROW_BYTES;
+    return page * ((int64_t)(ROWB + FP8_SCALE_BYTES) << a.page_shift) + rin * ROWB;
   } else {
     return (int64_t)slot * ROWB;
   }
@@ -613,13 +625,13 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         dma16<1 * 128>(g, mb + 1 * (S::RT * 128 - 128));
         dma16<2 * 128>(g, mb + 2 * (S::RT * 128 - 128));
         dma16<3 * 128>(g, mb + 3 * (S::RT * 128 - 128));
-        dma16<4 * 128>(g, mb + 4 * (S::RT * 128 - 128));
-        if constexpr (!S::FP8) {
+        if constexpr (S::NLINES > 4) dma16<4 * 128>(g, mb + 4 * (S::RT * 128 - 128));
+        if constexpr (S::NLINES > 5) {
           dma16<5 * 128>(g, mb + 5 * (S::RT * 128 - 128));
           dma16<6 * 128>(g, mb + 6 * (S::RT * 128 - 128));
           dma16<7 * 128>(g, mb + 7 * (S::RT * 128 - 128));
-          if constexpr (S::NLINES > 8) dma16<8 * 128>(g, mb + 8 * (S::RT * 128 - 128));
         }
+        if constexpr (S::NLINES > 8) dma16<8 * 128>(g, mb + 8 * (S::RT * 128 - 128));
       }
       if constexpr (S::FP8) {
         // the block scales of this wave's share of the tile rows, 16 B per row
@@ -631,8 +643,8 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
           const int slot = list[li];
           const int64_t page = slot >> a.page_shift;
           const int64_t rin = slot & ((1 << a.page_shift) - 1);
-          const uint8_t* g = a.kv + page * ((int64_t)FP8_SLOT_BYTES << a.page_shift) +
-                             ((int64_t)FP8_ROW_BYTES << a.page_shift) + rin * 16;
+          const uint8_t* g = a.kv + page * ((int64_t)(S::ROWB + FP8_SCALE_BYTES) << a.page_shift) +
+                             ((int64_t)S::ROWB << a.page_shift) + rin * FP8_SCALE_BYTES;
           dma16<0>(g, tl + S::BODY_BYTES + (uint32_t)(hg * SR * 16));
         }
       }
@@ -665,10 +677,12 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
             const u32x4 v = kq[2 * (kk >> 2) + ((kk & 3) >> 1)];
             kw[kk] = (kk & 1) ? u32x2{v[2], v[3]} : u32x2{v[0], v[1]};
           }
-          bf16x8 kr[2];
+          bf16x8 kr[2];   // rope k-steps (line group 4; none in the NoPE geometry)
+          if constexpr (!S::NOPE) {
 #pragma unroll
-          for (int kk = 0; kk < 2; ++kk)
-            kr[kk] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[f][kk] + 4 * S::RT * 128);
+            for (int kk = 0; kk < 2; ++kk)
+              kr[kk] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[f][kk] + 4 * S::RT * 128);
+          }
           __builtin_amdgcn_sched_barrier(0);
           // one accumulation chain per 128-dim block (interleaved, so consecutive
           // MFMAs are independent) and one per rope k-step
@@ -683,7 +697,8 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
               const int kk = 4 * blk + ks;
               ab[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(kw[kk][0], kw[kk][1]), qb[kk], ab[blk], 0, 0, 0);
             }
-            if (ks < 2) ar[ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks], qb[16 + ks], ar[ks], 0, 0, 0);
+            if constexpr (!S::NOPE)
+              if (ks < 2) ar[ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks], qb[16 + ks], ar[ks], 0, 0, 0);
           }
           f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -725,13 +740,14 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         }
       mx = fmaxf(mx, wave_xor(mx, 16));
       mx = fmaxf(mx, wave_xor(mx, 32));
-      // Fixed exponent reference: the first tile's max becomes the row's
-      // reference and later tiles use it unchanged (p <= 2^REF_HEADROOM), so
-      // the accumulators never need rescaling.  A tile that exceeds the
-      // reference by more than the headroom flags the work-group, which then
-      // recomputes the row once with its true maximum as the reference.
+      // Fixed exponent reference: the first tile's max, rounded up to an
+      // integer, becomes the row's reference and later tiles use it unchanged
+      // (p <= 2^REF_HEADROOM), so the accumulators never need rescaling.  A
+      // tile that exceeds the reference by more than the headroom flags the
+      // work-group, which then recomputes the row once with its true maximum
+      // (rounded up) as the reference.
       m_seen[0] = fmaxf(m_seen[0], mx);
-      if (m_run[0] == NEG_INF) m_run[0] = mx;
+      if (m_run[0] == NEG_INF) m_run[0] = int_ref(mx);
       overflow |= (mx > m_run[0] + REF_HEADROOM);
       float psum = 0.f;
       float pv[S::NF][4];
@@ -847,10 +863,12 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
 #pragma unroll
           for (int i = 0; i < 8; ++i)
             kq[i] = *reinterpret_cast<const LDS_AS u32x4*>(tp + kofs[f][i & 1] + (i >> 1) * S::RT * 128);
-          bf16x8 kr[2];
+          bf16x8 kr[2];   // rope k-steps (none in the NoPE geometry)
+          if constexpr (!S::NOPE) {
 #pragma unroll
-          for (int kk = 0; kk < 2; ++kk)
-            kr[kk] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[f][kk] + 4 * S::RT * 128);
+            for (int kk = 0; kk < 2; ++kk)
+              kr[kk] = *reinterpret_cast<const LDS_AS bf16x8*>(tp + kofs[f][kk] + 4 * S::RT * 128);
+          }
           f32x4 ab[4], ar[2];
 #pragma unroll
           for (int blk = 0; blk < 4; ++blk) ab[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -864,7 +882,8 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
               const bf16x8 kb = (ks & 1) ? fp8x8_to_bf16(v[2], v[3]) : fp8x8_to_bf16(v[0], v[1]);
               ab[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb[kk], ab[blk], 0, 0, 0);
             }
-            if (ks < 2) ar[ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks], qb[16 + ks], ar[ks], 0, 0, 0);
+            if constexpr (!S::NOPE)
+              if (ks < 2) ar[ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks], qb[16 + ks], ar[ks], 0, 0, 0);
           }
           f32x4 sc = ar[0] + ar[1];
 #pragma unroll
@@ -887,7 +906,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
           mex[wave * 64 + lane] = (m_run[0] == NEG_INF) ? mx : m_run[0];
           asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
           const float other = mex[(wave ^ 1) * 64 + lane];
-          if (m_run[0] == NEG_INF) m_run[0] = fmaxf(mx, other);
+          if (m_run[0] == NEG_INF) m_run[0] = int_ref(fmaxf(mx, other));
         }
         bf16x4 pb[4];   // P scaled by each 128-dim block's scale of the row
         if (active) {
@@ -1020,11 +1039,11 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
               const float other = mex[((wave ^ 1) * 2 + e) * 64 + lane];
-              if (m_run[e] == NEG_INF) m_run[e] = fmaxf(mx[e], other);
+              if (m_run[e] == NEG_INF) m_run[e] = int_ref(fmaxf(mx[e], other));
             }
           }
         } else {
-          if (m_run[0] == NEG_INF) m_run[0] = mx[0];
+          if (m_run[0] == NEG_INF) m_run[0] = int_ref(mx[0]);
         }
 #pragma unroll
         for (int e = 0; e < S::NE; ++e) {
@@ -1253,7 +1272,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
     LDS_AS float* mex = (LDS_AS float*)(lds + S::MEX_OFF);
     mex[wave * 64 + lane] = m_seen[0];
     __syncthreads();
-    m_run[0] = fmaxf(m_seen[0], mex[(wave ^ 1) * 64 + lane]);
+    m_run[0] = int_ref(fmaxf(m_seen[0], mex[(wave ^ 1) * 64 + lane]));
     __syncthreads();
   } else if constexpr (S::RSPLIT) {
     // the two waves holding a head's row halves take their common maximum
@@ -1262,10 +1281,10 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
     for (int e = 0; e < 2; ++e) mex[(wave * 2 + e) * 64 + lane] = m_seen[e];
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < 2; ++e) m_run[e] = fmaxf(m_seen[e], mex[((wave ^ 1) * 2 + e) * 64 + lane]);
+    for (int e = 0; e < 2; ++e) m_run[e] = int_ref(fmaxf(m_seen[e], mex[((wave ^ 1) * 2 + e) * 64 + lane]));
     __syncthreads();
   } else {
-    m_run[0] = m_seen[0];
+    m_run[0] = int_ref(m_seen[0]);
   }
 #pragma unroll
   for (int e = 0; e < S::NE; ++e) l_run[e] = 0.f;
@@ -1503,6 +1522,12 @@ using F_H1_B = Shape<1, 2, 32, 3, 1>;
 using F_H1_T = Shape<2, 1, 32, 3, 1, false, false, true>;   // one wave-pair stream: two per CU
 using F_H2_A = Shape<2, 1, 32, 4, 1>;
 using F_H4_A = Shape<4, 1, 32, 7, 1>;
+// fp8 NoPE geometry (rows of the 512 codes, no rope part): the fp8 shapes
+// (the 528-byte slots leave room for one more stage than the 656-byte ones)
+using NF_H1_A = Shape<2, 2, 32, 4, 1, false, false, true, false, true>;
+using NF_H1_T = Shape<2, 1, 32, 4, 1, false, false, true, false, true>;   // two per CU
+using NF_H2_A = Shape<2, 1, 32, 4, 1, false, false, false, false, true>;
+using NF_H4_A = Shape<4, 1, 32, 8, 1, false, false, false, false, true>;
 
 template <class S>
 FwdShape shape_of() {
@@ -1518,6 +1543,15 @@ hipError_t launch_one(const FwdArgs& a, int64_t grid, hipStream_t stream) {
 }  // namespace
 
 bool fwd_shape(int kv_format, int head_groups, int variant, int nope, FwdShape* shape) {
+  if (nope && kv_format == 1) {
+    if (!(variant == 0 || (variant == 2 && head_groups == 1))) return false;
+    switch (head_groups) {
+      case 1: *shape = variant == 2 ? shape_of<NF_H1_T>() : shape_of<NF_H1_A>(); return true;
+      case 2: *shape = shape_of<NF_H2_A>(); return true;
+      case 4: *shape = shape_of<NF_H4_A>(); return true;
+      default: return false;
+    }
+  }
   if (nope) {
     if (kv_format != 0 || !(variant == 0 || (variant == 2 && head_groups <= 2))) return false;
     switch (head_groups) {
@@ -1554,6 +1588,14 @@ bool fwd_shape(int kv_format, int head_groups, int variant, int nope, FwdShape* 
 
 hipError_t launch_fwd(const FwdArgs& a, int kv_format, int head_groups, int variant, int nope, int64_t grid,
                       hipStream_t stream) {
+  if (nope && kv_format == 1) {
+    switch (head_groups) {
+      case 1: return variant == 2 ? launch_one<NF_H1_T>(a, grid, stream) : launch_one<NF_H1_A>(a, grid, stream);
+      case 2: return launch_one<NF_H2_A>(a, grid, stream);
+      case 4: return launch_one<NF_H4_A>(a, grid, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   if (nope) {
     switch (head_groups) {
       case 1: return variant == 2 ? launch_one<N_H1_T>(a, grid, stream) : launch_one<N_H1_A>(a, grid, stream);

@@ -11,7 +11,7 @@ Workload shapes follow the pages' workloads:
     (vLLM PR #60220, "Claims": q is T x 64 x 576, out is T x 64 x 512;
     prhub report on vLLM PR #55738, "Key source snippets": nope part first,
     rope part last); with `rope_dims=0` the NoPE geometry: rows are the
-    512 latent dims alone (prhub report on vLLM PR #55738, "Details" items 1
+    512 latent dims alone (prhub report on vLLM PR #55738, "Implementation breakdown" items 1
     and 3: a zero-width rope part);
   * top-k = 2048 int32 indices per query row (vLLM PR #54951, "Summary");
   * the cache is paged, 64 tokens per page, and -1 marks a skipped entry
@@ -37,9 +37,10 @@ FP8_SCALE_BYTES = 4 * (D_LATENT // 128)         # four fp32 block scales
 SCALE_1_OVER_24 = float(np.float32(1.0 / 24.0))  # 1/sqrt(576) as the fp32 the kernel receives
 
 
-def fp8_page_bytes(page_size: int) -> int:
-    """Bytes of one page of the fp8 cache: P rows of [codes|rope], then P x 4 scales."""
-    return page_size * (FP8_ROW_BYTES + FP8_SCALE_BYTES)
+def fp8_page_bytes(page_size: int, rope_dims: int = D_ROPE) -> int:
+    """Bytes of one page of the fp8 cache: P rows of [codes|rope], then P x 4
+    scales (rope_dims 0: rows of the 512 codes alone)."""
+    return page_size * (D_LATENT + 2 * rope_dims + FP8_SCALE_BYTES)
 
 
 @dataclasses.dataclass
@@ -226,7 +227,7 @@ def build_case(name: str, *, seed: int, hist: list, new: list, num_heads: int, t
     contributes new[s] query rows at positions hist[s] .. hist[s] + new[s] - 1
     (unless `query_positions[s]` lists them explicitly).  rope_dims 0 draws
     the NoPE geometry (512-wide q and bf16 cache rows)."""
-    assert rope_dims in (0, D_ROPE) and (rope_dims == D_ROPE or kv_format == "bf16")
+    assert rope_dims in (0, D_ROPE)
     d_qk = D_LATENT + rope_dims
     rng = np.random.default_rng(seed)
     seq_lens = np.array([h + n for h, n in zip(hist, new)], dtype=np.int64)
@@ -266,7 +267,7 @@ def build_case(name: str, *, seed: int, hist: list, new: list, num_heads: int, t
         x = rng.standard_normal((nslots, D_LATENT), dtype=np.float32)
         x = x / np.repeat(scales, 128, axis=1)
         codes = to_e4m3_codes(x)
-        rope = normal_bf16(rng, (nslots, D_ROPE))
+        rope = normal_bf16(rng, (nslots, D_ROPE)) if rope_dims else None
         kv = pack_fp8_pages(codes, scales, rope, page_size)
     else:
         raise ValueError(kv_format)
@@ -276,18 +277,23 @@ def build_case(name: str, *, seed: int, hist: list, new: list, num_heads: int, t
                 fp8_codes=codes, fp8_scales=scales, fp8_rope=rope)
 
 
-def pack_fp8_pages(codes: np.ndarray, scales: np.ndarray, rope: np.ndarray, page_size: int) -> np.ndarray:
+def pack_fp8_pages(codes: np.ndarray, scales: np.ndarray, rope: Optional[np.ndarray], page_size: int) -> np.ndarray:
     """Write the fp8 cache's byte layout: page p = [P rows x (512 code bytes |
-    64 bf16 rope)] followed by [P rows x 4 fp32 scales]."""
+    64 bf16 rope)] followed by [P rows x 4 fp32 scales].  rope None: the NoPE
+    geometry, rows of the 512 code bytes alone."""
     nslots = codes.shape[0]
     assert nslots % page_size == 0
     npages = nslots // page_size
-    pb = fp8_page_bytes(page_size)
+    rope_dims = 0 if rope is None else D_ROPE
+    row_bytes = D_LATENT + 2 * rope_dims
+    pb = fp8_page_bytes(page_size, rope_dims)
     out = np.zeros((npages, pb), dtype=np.uint8)
-    rows = np.concatenate([codes.reshape(nslots, D_LATENT),
-                           rope.astype(np.uint16).view(np.uint8).reshape(nslots, 2 * D_ROPE)], axis=1)
-    out[:, :page_size * FP8_ROW_BYTES] = rows.reshape(npages, page_size * FP8_ROW_BYTES)
-    out[:, page_size * FP8_ROW_BYTES:] = scales.astype(np.float32).view(np.uint8).reshape(
+    parts = [codes.reshape(nslots, D_LATENT)]
+    if rope is not None:
+        parts.append(rope.astype(np.uint16).view(np.uint8).reshape(nslots, 2 * D_ROPE))
+    rows = np.concatenate(parts, axis=1)
+    out[:, :page_size * row_bytes] = rows.reshape(npages, page_size * row_bytes)
+    out[:, page_size * row_bytes:] = scales.astype(np.float32).view(np.uint8).reshape(
         npages, page_size * FP8_SCALE_BYTES)
     return out
 

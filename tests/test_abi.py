@@ -72,7 +72,8 @@ def test_zero_tokens_is_noop():
     (dict(kernel_variant=3, num_heads=32), B.SMLA_ERR_UNSUPPORTED),
     (dict(kernel_variant=2, geometry="nope", num_heads=64), B.SMLA_ERR_UNSUPPORTED),
     (dict(kernel_variant=3, num_heads=64), B.SMLA_ERR_UNSUPPORTED),
-    (dict(geometry="nope", kv_format="fp8"), B.SMLA_ERR_UNSUPPORTED),     # NoPE: bf16 caches only
+    (dict(geometry="nope", kv_format="fp8", kernel_variant=1), B.SMLA_ERR_UNSUPPORTED),
+    (dict(geometry="nope", kv_format="fp8", kernel_variant=2, num_heads=32), B.SMLA_ERR_UNSUPPORTED),
     (dict(geometry="nope", kernel_variant=1), B.SMLA_ERR_UNSUPPORTED),    # NoPE: default shapes only
     (dict(geometry="mla", q_strides=(8 * 512, 512)), B.SMLA_ERR_INVALID_ARG),   # 576-wide heads
     (dict(geometry="nope", q_strides=(8 * 512, 504)), B.SMLA_ERR_INVALID_ARG),
@@ -94,6 +95,10 @@ def test_geometry_values():
         pl = B.plan(pn, num_cus=256)
         assert pl.head_groups == (1 if h <= 16 else 2 if h <= 32 else 4)
         assert B.workspace_size(pn) == B.workspace_size(_params(num_heads=h))
+        # fp8 latent rows without a rope part
+        pf = _params(geometry="nope", num_heads=h, kv_format="fp8")
+        pl = B.plan(pf, num_cus=256)
+        assert pl.head_groups == (1 if h <= 16 else 2 if h <= 32 else 4)
 
 
 def _dense(p, q=16, kv=16, bt=16, qs=16, pos=16, out=16, lse=16):

@@ -69,6 +69,21 @@ def test_fp8_pack_layout():
     assert np.array_equal(kv[1, off:off + 16].view(np.float32), scales[s])
 
 
+def test_fp8_nope_pack_layout():
+    """NoPE fp8 pages: P rows of 512 code bytes, then P x 4 fp32 scales."""
+    rng = np.random.default_rng(3)
+    P = 16
+    n = 2 * P
+    codes = rng.integers(0, 256, size=(n, 512), dtype=np.uint8)
+    scales = rng.random((n, 4), dtype=np.float32)
+    kv = G.pack_fp8_pages(codes, scales, None, P)
+    assert kv.shape == (2, G.fp8_page_bytes(P, 0)) and G.fp8_page_bytes(64, 0) == 64 * 528
+    s = P + 7                                 # row 7 of page 1
+    assert np.array_equal(kv[1, 7 * 512:8 * 512], codes[s])
+    off = P * 512 + 7 * 16
+    assert np.array_equal(kv[1, off:off + 16].view(np.float32), scales[s])
+
+
 def test_e4m3_quantisation_saturates():
     x = np.array([0.0, 1.0, -3.3, 500.0, -1e6], dtype=np.float32)
     c = G.to_e4m3_codes(x)

@@ -89,7 +89,38 @@ def test_nope_equals_zero_rope_parts():
     np.testing.assert_allclose(out, out_p, rtol=1e-13, atol=1e-14)
     np.testing.assert_allclose(lse, lse_p, rtol=1e-13, atol=1e-14)
     with pytest.raises(ValueError):
-        O.gather_rows(c.kv, [0], "fp8", 64, d_qk=O.D_LATENT)
+        O.gather_rows(c.kv, [0], "bf16", 64, d_qk=520)
+
+
+def test_fp8_nope_equals_zero_rope_parts():
+    """An fp8 NoPE cache (rows of 512 scaled codes, no rope part) gives the
+    576-wide fp8 definition over the same codes and scales with a zero rope
+    part and zero rope dims of q.  The 576-wide cache is packed here from the
+    generator's components, so the oracle's two page readers (528- and
+    656-byte rows) must agree on every code and scale."""
+    c = G.make_mini(seed=16, num_heads=5, topk=150, num_seqs=2, tokens_per_seq=7, rope_dims=0, kv_format="fp8")
+    assert c.q.shape[2] == 512 and c.kv.shape[1] == G.fp8_page_bytes(c.page_size, 0) == c.page_size * 528
+    kw = dict(topk=c.topk, scale=c.scale, kv_format="fp8", page_size=c.page_size, index_mode="logical",
+              block_table=c.block_table, token_seq=c.token_seq)
+    out, lse = O.sparse_mla_forward(c.q, c.kv, c.topk_idx, **kw)
+    zero_rope = np.zeros((c.fp8_codes.shape[0], O.D_ROPE), np.uint16)
+    kv576 = G.pack_fp8_pages(c.fp8_codes, c.fp8_scales, zero_rope, c.page_size)
+    q576 = np.concatenate([c.q, np.zeros(c.q.shape[:-1] + (O.D_ROPE,), np.uint16)], axis=-1)
+    out_p, lse_p = O.sparse_mla_forward(q576, kv576, c.topk_idx, **kw)
+    np.testing.assert_allclose(out, out_p, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse, lse_p, rtol=1e-13, atol=1e-14)
+
+
+def test_fp8_nope_rows_dequant():
+    """The oracle's fp8 NoPE row reader against the generator's components,
+    dequantised with torch: value of dim d = float(code[d]) * scale[d // 128]."""
+    c = G.make_mini(seed=17, num_heads=8, topk=64, kv_format="fp8", page_size=16, rope_dims=0)
+    slots = np.array([0, 1, 15, 16, 17, c.num_slots - 1, 130], dtype=np.int64)
+    R = O.gather_rows(c.kv, slots, "fp8", c.page_size, d_qk=O.D_LATENT)
+    codes = torch.from_numpy(c.fp8_codes[slots]).view(torch.float8_e4m3fn).to(torch.float64)
+    sc = torch.from_numpy(c.fp8_scales[slots]).to(torch.float64).repeat_interleave(128, dim=1)
+    assert R.shape == (len(slots), 512)
+    assert np.array_equal(R, (codes * sc).numpy())
 
 
 def test_index_order_invariance():

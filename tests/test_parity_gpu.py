@@ -14,8 +14,8 @@ import torch
 
 from sparse_mla_attention_04_amd import binding as B
 from sparse_mla_attention_04_amd import inputs as G
-from tests.gpu_harness import (SPLIT_ATOL, Dev, check, check_bf16_pair, check_fp32_pair, merge_partials, oracle,
-                               run_gpu, run_partials, say, slot_indices, stratified_rows, to_np)
+from tests.gpu_harness import (SPLIT_ATOL, Dev, bf16_ulp, check, check_bf16_pair, check_fp32_pair, merge_partials,
+                               oracle, run_gpu, run_partials, say, slot_indices, stratified_rows, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -122,16 +122,21 @@ def test_page_permutation_bit_identical():
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
-@pytest.mark.parametrize("k", [1, 5, 300])
-def test_repeated_index_returns_row_exactly(k):
-    say("repeated index", k)
+@pytest.mark.parametrize("k,splits", [(1, 1), (5, 1), (300, 1), (300, 3)])
+def test_repeated_index_returns_the_row(k, splits):
+    """A list of k copies of one row returns that row's 512 latent dims: the
+    oracle exactly; the kernel within one bf16 ulp, since its P = 2^(x - m)
+    against an integer exponent reference m is rounded to bf16 (relative
+    error <= 2^-8) before P.V, while the normaliser sums the unrounded P."""
+    say("repeated index", k, splits)
     c = G.make_mini(seed=27, num_heads=16, topk=300)
     j = 77
     idx = np.full((c.num_tokens, k), j, dtype=np.int32)
     dev = Dev(c, idx=idx)
-    out, lse = to_np(*run_gpu(dev, logical=False, topk=k, num_splits=1))
+    out, lse = to_np(*run_gpu(dev, logical=False, topk=k, num_splits=splits))
     row = (c.kv.reshape(-1, 576)[j].astype(np.uint32) << 16).view(np.float32)[:512]
-    assert np.array_equal(out, np.broadcast_to(row, out.shape))
+    err = np.abs(out - row[None, None, :])
+    assert np.all(err <= bf16_ulp(row)[None, None, :]), "worst %.4g" % err.max()
     from oracle import sparse_mla_oracle as O
     ro, rl = O.sparse_mla_forward(c.q, c.kv, idx, topk=k, scale=c.scale, index_mode="slot")
     check(out, lse, ro, rl, "repeated index")
@@ -808,6 +813,49 @@ def test_nope_recompute_and_two_chunks(variant):
                      topk=2100, drop_frac=0.05, rope_dims=0)
     out, lse = to_np(*run_gpu(Dev(c), num_splits=1, variant=variant))
     check(out, lse, *oracle(c), what="nope topk 2100 v%d" % variant)
+
+
+@pytest.mark.parametrize("h,splits,variant,topk", [(8, 0, 0, 300), (8, 3, 0, 300), (16, 0, 2, 300), (12, 1, 2, 5000),
+                                                    (32, 0, 0, 300), (24, 2, 0, 300), (64, 0, 0, 300),
+                                                    (64, 4, 0, 300), (8, 1, 0, 40), (8, 1, 2, 5), (16, 1, 0, 70)])
+def test_nope_fp8_mini(h, splits, variant, topk):
+    """fp8 latent rows without a rope part (512 scaled codes) against the
+    oracle: every fp8 shape (wave pairs, two per CU, head-group waves),
+    splits, two compaction passes, lists of one to three tiles."""
+    say("nope fp8", h, splits, variant, topk)
+    c = G.make_mini(seed=75, num_heads=h, topk=topk, rope_dims=0, kv_format="fp8", drop_frac=0.2)
+    out, lse = to_np(*run_gpu(Dev(c), num_splits=splits, variant=variant))
+    check(out, lse, *oracle(c), what="nope fp8 h=%d s%d v%d topk %d" % (h, splits, variant, topk))
+
+
+@pytest.mark.parametrize("variant", [0, 2])
+def test_nope_fp8_slot_mode_page16_and_recompute(variant):
+    """fp8 NoPE: SLOT indices bit-identical to LOGICAL ones, pages of 16 rows
+    with a wide index buffer, and queries scaled by 64 (a score spread far
+    beyond the first tile's exponent headroom: the recomputation pass)."""
+    say("nope fp8 slot / P=16 / spread", variant)
+    c = G.make_mini(seed=76, num_heads=8, topk=256, rope_dims=0, kv_format="fp8", page_size=16, idx_stride=259)
+    dev = Dev(c)
+    o1, l1 = to_np(*run_gpu(dev, variant=variant))
+    check(o1, l1, *oracle(c), what="nope fp8 P=16 v%d" % variant)
+    o2, l2 = to_np(*run_gpu(Dev(c, idx=slot_indices(c)), logical=False, variant=variant))
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    qf = (c.q.astype(np.uint32) << 16).view(np.float32)
+    c2 = G.Case(**{**c.__dict__, "q": G.to_bf16_bits(qf * 64.0)})
+    for splits in (1, 2):
+        out, lse = to_np(*run_gpu(Dev(c2), num_splits=splits, variant=variant))
+        check(out, lse, *oracle(c2), what="nope fp8 spread s%d v%d" % (splits, variant))
+
+
+def test_nope_fp8_large_batch_sampled():
+    """A c5-shaped batch (16 sequences, histories 8192..131072, 2048 new rows
+    each, h = 8, top-k 2048) with fp8 NoPE rows, on a stratified subset of
+    2048 rows."""
+    say("nope fp8 c5-shaped")
+    c = G.make_config("c5_fp8", rope_dims=0)
+    out, lse = to_np(*run_gpu(Dev(c)))
+    rows = stratified_rows(c, 2048, seed=7)
+    check(out[rows], lse[rows], *oracle(c, rows=rows), what="nope fp8 c5 (%d rows)" % len(rows))
 
 
 # --------------------------------------------------------------------------- dense causal mode
