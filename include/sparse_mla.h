@@ -224,6 +224,24 @@ int sparse_mla_fwd(const smla_params* p, const void* q, const void* kv_cache,
                    const int32_t* topk_idx, void* out, float* lse,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* sparse_mla_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The split partials go to a static
+ * device array of SMLA_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends (looked up on the first call per
+ * device; nothing is allocated per call).  Same arguments, plan, kernels,
+ * results and validation as sparse_mla_fwd; a plan whose partials exceed
+ * the static array (a forced num_splits with T * num_splits * h * 513 * 4 >
+ * SMLA_NOALLOC_SCRATCH_BYTES; every automatic plan on up to 256 compute
+ * units fits) returns SMLA_ERR_WORKSPACE_TOO_SMALL with nothing enqueued.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (on different streams) race and must not be issued; stream-ordered
+ * calls are safe, since every partial is written before it is read. */
+#define SMLA_NOALLOC_SCRATCH_BYTES ((size_t)256 * 64 * 513 * 4)
+int sparse_mla_fwd_noalloc(const smla_params* p, const void* q, const void* kv_cache,
+                           const int32_t* block_table, const int32_t* token_seq,
+                           const int32_t* topk_idx, void* out, float* lse, void* stream);
+
 /* The attention kernel alone, leaving the split results unmerged: for every
  * query row t and KV split s < S (S = the plan's num_splits; 1 when unsplit)
  * it writes the split's normalised fp32 output and its lse to the workspace,

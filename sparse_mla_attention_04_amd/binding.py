@@ -31,7 +31,7 @@ D_QK, D_V = 576, 512
 
 EXPORTS = ("sparse_mla_workspace_size", "sparse_mla_plan", "sparse_mla_plan_for",
            "sparse_mla_fwd", "sparse_mla_fwd_partials", "sparse_mla_lse_combine",
-           "sparse_mla_status_string", "sparse_mla_dense_fwd", "sparse_mla_topk")
+           "sparse_mla_status_string", "sparse_mla_dense_fwd", "sparse_mla_topk", "sparse_mla_fwd_noalloc")
 
 
 class Params(ctypes.Structure):
@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
         L.sparse_mla_fwd.argtypes = [ctypes.POINTER(Params)] + [ctypes.c_void_p] * 7 + \
             [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.sparse_mla_fwd.restype = ctypes.c_int
+        L.sparse_mla_fwd_noalloc.argtypes = [ctypes.POINTER(Params)] + [ctypes.c_void_p] * 8
+        L.sparse_mla_fwd_noalloc.restype = ctypes.c_int
         L.sparse_mla_fwd_partials.argtypes = [ctypes.POINTER(Params)] + [ctypes.c_void_p] * 6 + \
             [ctypes.c_size_t, ctypes.c_void_p]
         L.sparse_mla_fwd_partials.restype = ctypes.c_int
@@ -206,6 +208,23 @@ def fwd(q, kv, topk_idx, out, lse, *, topk: int, scale: float, workspace=None, p
                               ctypes.c_void_p(int(stream)))
     if rc != SMLA_OK:
         raise SparseMLAError(rc, "sparse_mla_fwd")
+
+
+def fwd_noalloc(q, kv, topk_idx, out, lse, *, topk: int, scale: float, page_size: int = 64,
+                kv_format: str = "bf16", block_table=None, token_seq=None, tiling: str = "auto",
+                num_splits: int = 0, kernel_variant: int = 0, stream=None, params: Optional[Params] = None) -> None:
+    """sparse_mla_fwd_noalloc on torch tensors: sparse_mla_fwd with the split
+    partials in the library's static device scratch (no workspace argument)."""
+    import torch
+    p = params or params_for(q, kv, topk_idx, out, lse, topk=topk, scale=scale, page_size=page_size,
+                             kv_format=kv_format, block_table=block_table, token_seq=token_seq,
+                             tiling=tiling, num_splits=num_splits, kernel_variant=kernel_variant)
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    rc = lib().sparse_mla_fwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(kv), _ptr(block_table), _ptr(token_seq),
+                                      _ptr(topk_idx), _ptr(out), _ptr(lse), ctypes.c_void_p(int(stream)))
+    if rc != SMLA_OK:
+        raise SparseMLAError(rc, "sparse_mla_fwd_noalloc")
 
 
 def dense_fwd(q, kv, out, lse, *, block_table, query_start, positions, scale: float, page_size: int = 64,

@@ -296,6 +296,17 @@ int sparse_mla_fwd(const smla_params* p, const void* q, const void* kv_cache, co
              workspace_bytes, stream);
 }
 
+int sparse_mla_fwd_noalloc(const smla_params* p, const void* q, const void* kv_cache, const int32_t* block_table,
+                           const int32_t* token_seq, const int32_t* topk_idx, void* out, float* lse, void* stream) {
+  int rc = check_params(p);
+  if (rc != SMLA_OK) return rc;
+  if (p->num_tokens == 0) return SMLA_OK;
+  void* ws = nullptr;
+  if (smla::noalloc_scratch(&ws) != hipSuccess) return SMLA_ERR_HIP;
+  return run(Mode::kFull, p, q, kv_cache, block_table, token_seq, topk_idx, out, lse, ws,
+             smla::kNoallocScratchBytes, stream);
+}
+
 int sparse_mla_fwd_partials(const smla_params* p, const void* q, const void* kv_cache,
                             const int32_t* block_table, const int32_t* token_seq, const int32_t* topk_idx,
                             void* workspace, size_t workspace_bytes, void* stream) {

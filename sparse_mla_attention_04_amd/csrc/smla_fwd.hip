@@ -33,9 +33,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "smla_internal.h"
+
+// Device scratch of the allocation-free entry point: the fp32 split partials
+// of one call (units x h x 513 fp32).  Each GPU the library runs on holds its
+// own copy until the process ends; host code never uses this name as an
+// address, only the per-device pointer hipGetSymbolAddress returns for it.
+static __device__ __align__(256) uint8_t scratch[smla::kNoallocScratchBytes];
 
 namespace smla {
 namespace {
@@ -1635,6 +1642,27 @@ hipError_t launch_dense(const FwdArgs& a, int nope, int64_t grid, hipStream_t st
   return nope ? launch_one<D_H4_N>(a, grid, stream) : launch_one<D_H4>(a, grid, stream);
 }
 int dense_lds_bytes(int nope) { return nope ? D_H4_N::LDS_BYTES : D_H4::LDS_BYTES; }
+
+// Device address of this GPU's `scratch` array (the current device's), looked
+// up once per device with that device current and kept.
+hipError_t noalloc_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)a.T, (unsigned)((a.h * 64 + 255) / 256));

@@ -9,6 +9,17 @@ namespace smla {
 // in LDS per pass.
 constexpr int kListCap = 2048;
 
+// Bytes of the static device scratch of the allocation-free entry point:
+// 256 split units x 64 heads x 513 fp32, the largest partials buffer of any
+// automatic plan on a GPU of up to 256 compute units (an automatic plan
+// splits only when T < #CU, and then into at most #CU units).
+constexpr size_t kNoallocScratchBytes = (size_t)256 * 64 * 513 * 4;
+constexpr int kMaxDevices = 256;
+
+// This GPU's copy of the static scratch (the current device), looked up on
+// the first call per device; never freed.
+hipError_t noalloc_scratch(void** ptr);
+
 // Everything a forward launch needs, passed by value as the kernel argument.
 struct FwdArgs {
   const uint16_t* q;          // bf16 [T, h, 576] (strided)
