@@ -31,6 +31,8 @@ Workloads (synthetic, seeded; `--workload` runs one of them alone):
                        from position 0, h=8 (every prefix within top-k)
   topk_4096x65536      the per-row top-k selection: 4096 rows of 65536 fp32 scores
                        (N(0,1) from a seeded device generator), k = 2048
+  indexer_4096x65536   the indexer step: MQA logits (64 heads x 128 dims) of 4096 rows against
+                       their causal 65536-key history, then top-k 2048
 """
 from __future__ import annotations
 
@@ -409,6 +411,68 @@ DTYPE_NOTE = {"fp8_e4m3+bf16": "fp8 e4m3 latent cache dequantised exactly to bf1
               "bf16": "bf16 cache and MFMA with fp32 accumulation and fp32 softmax"}
 
 
+def bench_indexer(args):
+    """The indexer step: MQA logits (sparse_mla_indexer_logits) then top-k
+    (sparse_mla_topk) for 4096 query rows at the last positions of a
+    65536-key history, H = 64 heads of 128 dims, k = 2048.  The logits kernel
+    is MFMA-bound: algorithmic flops 2 * H * 128 per (row, history key)."""
+    import torch
+    from sparse_mla_attention_04_amd import binding as B
+    from sparse_mla_attention_04_amd import inputs as G
+    c = G.make_indexer_case("indexer_4096x65536", seed=1008, num_rows=4096, n_keys=65536, num_heads=64)
+    T, N, H = c.num_rows, c.n_keys, c.num_heads
+    q = torch.from_numpy(c.q.view(np.int16)).cuda().view(torch.bfloat16)
+    k = torch.from_numpy(c.k.view(np.int16)).cuda().view(torch.bfloat16)
+    w = torch.from_numpy(c.w).cuda()
+    lens = torch.from_numpy(c.lens).cuda()
+    logits = torch.empty((T, N), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, c.topk), dtype=torch.int32, device="cuda")
+
+    def logits_only():
+        B.indexer_logits(q, k, w, logits, lens=lens)
+
+    def step():
+        logits_only()
+        B.topk(logits, c.topk, lens=lens, out=idx)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    K2 = max(20, min(args.steps, 200))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K2)]
+    for a_, b_ in evs:
+        a_.record()
+        logits_only()
+        b_.record()
+    torch.cuda.synchronize()
+    kern = np.array([a_.elapsed_time(b_) for a_, b_ in evs])
+    kern_ms = float(np.mean(kern))
+    pairs = int(np.clip(c.lens, 0, N).astype(np.int64).sum())
+    flops = pairs * H * 128 * 2
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    res = {"metric": "sparse MLA indexer (MQA logits + top-k): query rows/s", "value": round(T / (ms * 1e-3), 1),
+           "unit": "query-rows/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic (seeded N(0,1) q, k; N(0,1)/sqrt(H) weights)",
+           "config": {"workload": "indexer_4096x65536", "num_rows": T, "n_keys": N, "num_heads": H,
+                      "head_dim": 128, "topk": c.topk, "lens": "causal: positions 61440..65535 + 1"},
+           "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                        "kernel": "smla_indexer_logits", "kernel_us": round(kern_ms * 1e3, 2),
+                        "kernel_us_p10_p50_p90": [round(float(np.percentile(kern, q_)) * 1e3, 2) for q_ in (10, 50, 90)],
+                        "algorithmic_flops": flops,
+                        "per_unit": "one (row, history key) pair: 2 x H x 128 flop"},
+           "topk_us_per_step": round(ms * 1e3 - kern_ms * 1e3, 2)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -426,6 +490,8 @@ def main():
         return
     if args.workload == "topk_4096x65536":
         return bench_topk(args)
+    if args.workload == "indexer_4096x65536":
+        return bench_indexer(args)
 
     headline = args.workload == "headline"
     main_name = "c5_fp8" if headline else args.workload

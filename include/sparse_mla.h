@@ -313,6 +313,38 @@ int sparse_mla_dense_fwd(const smla_params* p, const void* q, const void* kv_cac
 int sparse_mla_topk(const float* scores, int64_t ld, const int32_t* lens, int32_t num_rows,
                     int32_t n_keys, int32_t k, int32_t* idx, int64_t idx_stride, void* stream);
 
+/* Indexer scoring, the step before sparse_mla_topk: MQA logits of every
+ * query row against its key history (vLLM PR #54951, "TL;DR" and
+ * "Summary": each row is scored against the full available key history,
+ * then top-k; "Additional checks": valid logits of a row are the same
+ * whatever other rows share the batch).  The pages do not give the head
+ * count, head width or head reduction; this library computes
+ *     logits[t, s] = sum_j w[t, j] * max(0, q[t, j, :] . k[s, :]),  s < lens[t]
+ * (per-head ReLU, then a sum weighted by per-row head weights: the form of
+ * the MQA-logits kernel those checks run), with every indexer head of a row
+ * sharing one key per history position (MQA).
+ *   q       bf16 [num_rows, num_heads, head_dim] (device), element strides
+ *           q_stride_t / q_stride_h (multiples of 8; 16-B aligned)
+ *   k       bf16 [n_keys, head_dim] (device), row stride k_stride elements
+ *           (multiple of 8; 16-B aligned): token keys, or pooled keys when
+ *           the caller pools its history
+ *   w       fp32 [num_rows, num_heads] (device), row stride w_stride_t
+ *           (multiple of 4; 16-B aligned)
+ *   lens    int32 [num_rows] (device) or NULL: row t scores keys
+ *           0 .. lens[t] - 1 (clamped to [0, n_keys]); NULL: all n_keys
+ *   logits  fp32 [num_rows, ld] (device, ld >= n_keys): columns s < lens[t]
+ *           are written, the others are left untouched
+ * head_dim must be SMLA_INDEXER_HEAD_DIM and num_heads a multiple of 16 up
+ * to 64 (else SMLA_ERR_UNSUPPORTED).  Sizes / strides / pointers as stated
+ * or SMLA_ERR_INVALID_ARG (nothing launched).  Enqueued on `stream`; no
+ * allocation, no synchronisation.  The logits feed sparse_mla_topk (scores =
+ * logits, ld, lens) to produce the index lists. */
+#define SMLA_INDEXER_HEAD_DIM 128
+int sparse_mla_indexer_logits(const void* q, int64_t q_stride_t, int64_t q_stride_h, const void* k,
+                              int64_t k_stride, const float* w, int64_t w_stride_t, const int32_t* lens,
+                              int32_t num_rows, int32_t n_keys, int32_t num_heads, int32_t head_dim,
+                              float* logits, int64_t ld, void* stream);
+
 /* Static, human-readable text for a status code. */
 const char* sparse_mla_status_string(int status);
 

@@ -31,7 +31,8 @@ D_QK, D_V = 576, 512
 
 EXPORTS = ("sparse_mla_workspace_size", "sparse_mla_plan", "sparse_mla_plan_for",
            "sparse_mla_fwd", "sparse_mla_fwd_partials", "sparse_mla_lse_combine",
-           "sparse_mla_status_string", "sparse_mla_dense_fwd", "sparse_mla_topk", "sparse_mla_fwd_noalloc")
+           "sparse_mla_status_string", "sparse_mla_dense_fwd", "sparse_mla_topk", "sparse_mla_fwd_noalloc",
+           "sparse_mla_indexer_logits")
 
 
 class Params(ctypes.Structure):
@@ -107,6 +108,11 @@ def lib() -> ctypes.CDLL:
                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
                                       ctypes.c_void_p]
         L.sparse_mla_topk.restype = ctypes.c_int
+        L.sparse_mla_indexer_logits.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                                ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        L.sparse_mla_indexer_logits.restype = ctypes.c_int
         L.sparse_mla_status_string.argtypes = [ctypes.c_int]
         L.sparse_mla_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -265,6 +271,23 @@ def topk(scores, k: int, *, lens=None, out=None, stream=None):
     if rc != SMLA_OK:
         raise SparseMLAError(rc, "sparse_mla_topk")
     return out
+
+
+def indexer_logits(q, k, w, logits, *, lens=None, stream=None) -> None:
+    """sparse_mla_indexer_logits on torch tensors: q bf16 [T, H, 128] (last dim
+    contiguous), k bf16 [N, 128] (rows contiguous), w fp32 [T, H], logits fp32
+    [T, >= N] (written for keys < lens[t]), lens int32 [T] or None."""
+    import torch
+    T, H, D = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
+    N = int(k.shape[0])
+    assert q.stride(2) == 1 and k.stride(1) == 1 and w.stride(1) == 1 and logits.stride(1) == 1
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    rc = lib().sparse_mla_indexer_logits(_ptr(q), int(q.stride(0)), int(q.stride(1)), _ptr(k), int(k.stride(0)),
+                                         _ptr(w), int(w.stride(0)), _ptr(lens), T, N, H, D, _ptr(logits),
+                                         int(logits.stride(0)), ctypes.c_void_p(int(stream)))
+    if rc != SMLA_OK:
+        raise SparseMLAError(rc, "sparse_mla_indexer_logits")
 
 
 def fwd_partials(q, kv, topk_idx, workspace, *, topk: int, scale: float, page_size: int = 64,

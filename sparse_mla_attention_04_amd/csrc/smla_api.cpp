@@ -417,6 +417,47 @@ int sparse_mla_topk(const float* scores, int64_t ld, const int32_t* lens, int32_
   return SMLA_OK;
 }
 
+int sparse_mla_indexer_logits(const void* q, int64_t q_stride_t, int64_t q_stride_h, const void* k, int64_t k_stride,
+                              const float* w, int64_t w_stride_t, const int32_t* lens, int32_t num_rows,
+                              int32_t n_keys, int32_t num_heads, int32_t head_dim, float* logits, int64_t ld,
+                              void* stream) {
+  if (num_rows < 0 || n_keys < 0 || num_heads < 1 || head_dim < 1) return SMLA_ERR_INVALID_ARG;
+  if (head_dim != SMLA_INDEXER_HEAD_DIM || num_heads % 16 != 0 || num_heads > SMLA_MAX_HEADS)
+    return SMLA_ERR_UNSUPPORTED;
+  if (q_stride_h < head_dim || q_stride_h % 8 || q_stride_t < 0 || q_stride_t % 8 || k_stride < head_dim ||
+      k_stride % 8 || w_stride_t < 0 || w_stride_t % 4 || ld < n_keys)
+    return SMLA_ERR_INVALID_ARG;
+  if (num_rows > 1 && (q_stride_t < (int64_t)(num_heads - 1) * q_stride_h + head_dim || w_stride_t < num_heads))
+    return SMLA_ERR_INVALID_ARG;
+  if (num_rows == 0 || n_keys == 0) return SMLA_OK;
+  if (!q || !k || !w || !logits) return SMLA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(w, 16) || !aligned(logits, 4) || (lens && !aligned(lens, 4)))
+    return SMLA_ERR_INVALID_ARG;
+  constexpr int kChunkKeys = 4096;
+  smla::IndexerArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.w = w;
+  a.lens = lens;
+  a.logits = logits;
+  a.q_st = q_stride_t;
+  a.q_sh = q_stride_h;
+  a.k_st = k_stride;
+  a.w_st = w_stride_t;
+  a.ld = ld;
+  a.T = num_rows;
+  a.n_keys = n_keys;
+  a.H = num_heads;
+  a.chunk_keys = kChunkKeys;
+  const int rpb = smla::indexer_rows_per_block();
+  a.row_blocks = (num_rows + rpb - 1) / rpb;
+  a.units = (int64_t)a.row_blocks * ((n_keys + kChunkKeys - 1) / kChunkKeys);
+  const int64_t grid = (a.units + 7) / 8 * 8;
+  a.grid_per_xcd = (int32_t)(grid / 8);
+  if (smla::launch_indexer(a, grid, static_cast<hipStream_t>(stream)) != hipSuccess) return SMLA_ERR_HIP;
+  return SMLA_OK;
+}
+
 const char* sparse_mla_status_string(int status) {
   switch (status) {
     case SMLA_OK: return "ok";

@@ -66,6 +66,21 @@ struct TopkArgs {
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 
+// Indexer scoring (MQA logits): one work-group per (8 query rows, key chunk).
+struct IndexerArgs {
+  const uint16_t* q;          // bf16 [T, H, 128] (strided)
+  const uint16_t* k;          // bf16 [n_keys, 128] (row stride k_st)
+  const float* w;             // fp32 [T, H] (row stride w_st)
+  const int32_t* lens;        // int32 [T] or null (every row sees n_keys keys)
+  float* logits;              // fp32 [T, ld]
+  int64_t q_st, q_sh, k_st, w_st, ld;
+  int64_t units;              // row_blocks * key chunks
+  int32_t row_blocks, chunk_keys, grid_per_xcd;
+  int32_t T, n_keys, H;
+};
+hipError_t launch_indexer(const IndexerArgs& a, int64_t grid, hipStream_t stream);
+int indexer_rows_per_block();
+
 // Pipeline shape of one forward kernel instantiation.
 struct FwdShape {
   int head_groups, row_groups, tile_rows, stages, threads, lds_bytes;

@@ -371,3 +371,57 @@ class DeviceCase:
         self.idx = torch.from_numpy(np.ascontiguousarray(case.topk_idx if idx is None else idx)).to(device)
         self.bt = torch.from_numpy(case.block_table).to(device)
         self.ts = torch.from_numpy(case.token_seq).to(device)
+
+
+# ----------------------------------------------------------------------------
+# the indexer's scoring step (MQA logits -> top-k)
+# ----------------------------------------------------------------------------
+
+INDEXER_HEAD_DIM = 128
+
+
+@dataclasses.dataclass
+class IndexerCase:
+    """One synthetic indexer batch (host arrays).
+
+    q     uint16 [T, H, 128]  bf16 query of each indexer head of a row
+    k     uint16 [N, 128]     bf16 key of each history position (shared by the heads)
+    w     fp32   [T, H]       per-row head weights
+    lens  int32  [T]          keys a row scores: its causal history p_t + 1
+    """
+    name: str
+    q: np.ndarray
+    k: np.ndarray
+    w: np.ndarray
+    lens: np.ndarray
+    topk: int
+
+    @property
+    def num_rows(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def num_heads(self) -> int:
+        return int(self.q.shape[1])
+
+    @property
+    def n_keys(self) -> int:
+        return int(self.k.shape[0])
+
+
+def make_indexer_case(name: str, *, seed: int, num_rows: int, n_keys: int, num_heads: int = 64,
+                      topk: int = 2048, positions: Optional[np.ndarray] = None) -> IndexerCase:
+    """Query rows at the last `num_rows` positions of an `n_keys`-token history
+    (a prefill chunk on top of its history) unless `positions` are given;
+    q and k N(0,1) rounded to bf16, head weights N(0,1) / sqrt(H) in fp32.
+    Draw order: positions -> q -> k -> w."""
+    rng = np.random.default_rng(seed)
+    if positions is None:
+        positions = np.arange(n_keys - num_rows, n_keys, dtype=np.int64)
+    positions = np.asarray(positions, dtype=np.int64)
+    lens = (positions + 1).astype(np.int32)
+    q = normal_bf16(rng, (num_rows, num_heads, INDEXER_HEAD_DIM))
+    k = normal_bf16(rng, (n_keys, INDEXER_HEAD_DIM))
+    w = (rng.standard_normal((num_rows, num_heads), dtype=np.float32) / np.float32(np.sqrt(num_heads))).astype(
+        np.float32)
+    return IndexerCase(name=name, q=q, k=k, w=w, lens=lens, topk=topk)

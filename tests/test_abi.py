@@ -258,3 +258,29 @@ def test_topk_bad_args_rejected(kw):
 
 def test_topk_empty_batch_is_ok():
     assert _topk(rows=0, scores=None, idx=None) == B.SMLA_OK
+
+
+def _ix(**kw):
+    a = dict(q=16, qst=64 * 128, qsh=128, k=16, kst=128, w=16, wst=64, lens=None, T=4, N=100, H=64, D=128,
+             out=16, ld=100)
+    a.update(kw)
+    L = B.lib()
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return L.sparse_mla_indexer_logits(v(a["q"]), a["qst"], a["qsh"], v(a["k"]), a["kst"], v(a["w"]), a["wst"],
+                                       v(a["lens"]), a["T"], a["N"], a["H"], a["D"], v(a["out"]), a["ld"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=64), B.SMLA_ERR_UNSUPPORTED), (dict(H=24), B.SMLA_ERR_UNSUPPORTED), (dict(H=80), B.SMLA_ERR_UNSUPPORTED),
+    (dict(H=0), B.SMLA_ERR_INVALID_ARG), (dict(T=-1), B.SMLA_ERR_INVALID_ARG), (dict(ld=99), B.SMLA_ERR_INVALID_ARG),
+    (dict(qsh=120), B.SMLA_ERR_INVALID_ARG), (dict(kst=130), B.SMLA_ERR_INVALID_ARG), (dict(wst=62), B.SMLA_ERR_INVALID_ARG),
+    (dict(q=8), B.SMLA_ERR_INVALID_ARG), (dict(w=None), B.SMLA_ERR_INVALID_ARG), (dict(out=2), B.SMLA_ERR_INVALID_ARG),
+    (dict(qst=64 * 128 - 8), B.SMLA_ERR_INVALID_ARG),
+])
+def test_indexer_bad_args_rejected(kw, code):
+    assert _ix(**kw) == code
+
+
+def test_indexer_empty_is_ok():
+    assert _ix(T=0, q=None, k=None, w=None, out=None) == B.SMLA_OK
+    assert _ix(N=0, ld=0, q=None, k=None, w=None, out=None) == B.SMLA_OK
