@@ -1010,68 +1010,96 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
       // back as pb[4q + j].  With RSPLIT, `first` (work-group uniform) sets the
       // exponent reference of each head from the tile's maximum over both
       // row halves, exchanged with the partner wave through LDS.
-      auto softmax = [&](int it, const f32x4* scv, bool first) -> bf16x8 {
+      // The softmax runs in stages so that, in a pipeline step, each stage
+      // can sit between two groups of P.V MFMAs (which do not depend on it):
+      //   sm_scale(q): scale and mask fragment q, partial maximum;
+      //   sm_reduce:   maximum over the lanes sharing a head, reference, overflow;
+      //   sm_exp(q):   P of fragment q and its row sum;
+      //   sm_finish:   row sums into l_run.
+      struct SmState {
+        float x[2][4];
+        float mx[2];
+        float psum[2];
+        bf16x8 pb;
+      };
+      auto sm_init = [&](SmState& st) {
+        st.mx[0] = st.mx[1] = NEG_INF;
+        st.psum[0] = st.psum[1] = 0.f;
+      };
+      auto sm_scale = [&](int it, const f32x4* scv, int q, SmState& st) {
         const int left = n_valid - it * S::RT;
         // dense mode: positions past the slot's own row, or on an invalid
         // page (pages hold >= 16 rows, so a 16-row fragment has one page)
-        bool pgok[2] = {true, true};
+        bool pgok = true;
         if constexpr (S::DENSE) {
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int p0 = it * S::RT + 16 * q;
-            pgok[q] = p0 < n_valid && list[p0 >> a.page_shift] >= 0;
-          }
+          const int p0 = it * S::RT + 16 * q;
+          pgok = p0 < n_valid && list[p0 >> a.page_shift] >= 0;
         }
-        float x[2][4];
-        float mx[2] = {NEG_INF, NEG_INF};
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+        for (int j = 0; j < 4; ++j) {
+          const int row = (S::RSPLIT ? 16 * (wave & 1) : 16 * q) + 4 * g4 + j;
+          const float v = scv[q][j] * a.scale_log2;
+          const bool keep = S::DENSE ? (pgok && it * S::RT + row <= d_plim) : (row < left);
+          st.x[q][j] = keep ? v : NEG_INF;
+          st.mx[S::RSPLIT ? q : 0] = fmaxf(st.mx[S::RSPLIT ? q : 0], st.x[q][j]);
+        }
+      };
+      auto sm_reduce = [&](SmState& st, bool first) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int row = (S::RSPLIT ? 16 * (wave & 1) : 16 * q) + 4 * g4 + j;
-            const float v = scv[q][j] * a.scale_log2;
-            const bool keep = S::DENSE ? (pgok[q] && it * S::RT + row <= d_plim) : (row < left);
-            x[q][j] = keep ? v : NEG_INF;
-            mx[S::RSPLIT ? q : 0] = fmaxf(mx[S::RSPLIT ? q : 0], x[q][j]);
-          }
-#pragma unroll
-        for (int e = 0; e < S::NE; ++e) mx[e] = max_xor16_32(mx[e]);
+        for (int e = 0; e < S::NE; ++e) st.mx[e] = max_xor16_32(st.mx[e]);
         if constexpr (S::RSPLIT) {
           if (first) {
             // in exchange buffer 1: buffer 0 receives P of this tile right after
             LDS_AS float* mex = (LDS_AS float*)(lds + S::PEX_OFF + 4096);
 #pragma unroll
-            for (int e = 0; e < 2; ++e) mex[(wave * 2 + e) * 64 + lane] = (m_run[e] == NEG_INF) ? mx[e] : m_run[e];
+            for (int e = 0; e < 2; ++e) mex[(wave * 2 + e) * 64 + lane] = (m_run[e] == NEG_INF) ? st.mx[e] : m_run[e];
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
               const float other = mex[((wave ^ 1) * 2 + e) * 64 + lane];
-              if (m_run[e] == NEG_INF) m_run[e] = int_ref(fmaxf(mx[e], other));
+              if (m_run[e] == NEG_INF) m_run[e] = int_ref(fmaxf(st.mx[e], other));
             }
           }
         } else {
-          if (m_run[0] == NEG_INF) m_run[0] = int_ref(mx[0]);
+          if (m_run[0] == NEG_INF) m_run[0] = int_ref(st.mx[0]);
         }
 #pragma unroll
         for (int e = 0; e < S::NE; ++e) {
-          m_seen[e] = fmaxf(m_seen[e], mx[e]);
-          overflow |= (mx[e] > m_run[e] + REF_HEADROOM);
+          m_seen[e] = fmaxf(m_seen[e], st.mx[e]);
+          overflow |= (st.mx[e] > m_run[e] + REF_HEADROOM);
         }
-        bf16x8 pb;
-        float psum[2] = {0.f, 0.f};
+      };
+      auto sm_exp = [&](int q, SmState& st) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+        for (int j = 0; j < 4; ++j) {
+          float pj = fast_exp2(st.x[q][j] - m_run[S::RSPLIT ? q : 0]);
+          // dense mode: a slot may see no valid position yet (reference unset)
+          if constexpr (S::DENSE) pj = (m_run[0] == NEG_INF) ? 0.f : pj;
+          st.psum[S::RSPLIT ? q : 0] += pj;
+          st.pb[4 * q + j] = (__bf16)pj;
+        }
+      };
+      auto sm_finish = [&](SmState& st) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float pj = fast_exp2(x[q][j] - m_run[S::RSPLIT ? q : 0]);
-            // dense mode: a slot may see no valid position yet (reference unset)
-            if constexpr (S::DENSE) pj = (m_run[0] == NEG_INF) ? 0.f : pj;
-            psum[S::RSPLIT ? q : 0] += pj;
-            pb[4 * q + j] = (__bf16)pj;
-          }
-#pragma unroll
-        for (int e = 0; e < S::NE; ++e) l_run[e] += psum[e];
-        return pb;
+        for (int e = 0; e < S::NE; ++e) l_run[e] += st.psum[e];
+      };
+      // online softmax of one tile (base 2, fixed exponent reference).  The
+      // lane owns head n of a 16-head group and rows 4*g4 + j of a 16-row
+      // fragment: scv[q] is fragment q (rows 16q + ..) of the wave's group, or
+      // with RSPLIT head group q of the wave's rows 16*(wave & 1) + ..; P comes
+      // back as pb[4q + j].  With RSPLIT, `first` (work-group uniform) sets the
+      // exponent reference of each head from the tile's maximum over both
+      // row halves, exchanged with the partner wave through LDS.
+      auto softmax = [&](int it, const f32x4* scv, bool first) -> bf16x8 {
+        SmState st;
+        sm_init(st);
+        sm_scale(it, scv, 0, st);
+        sm_scale(it, scv, 1, st);
+        sm_reduce(st, first);
+        sm_exp(0, st);
+        sm_exp(1, st);
+        sm_finish(st);
+        return st.pb;
       };
       // scores of tile itq (K operands through a ring of KRING reads) with the
       // gathers of tile itd interleaved, one 128-B line per four MFMAs
@@ -1202,20 +1230,30 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
           // P.V of tile it over this wave's 8 output fragments x 4 head groups;
           // each fragment's V^T registers are refilled from tile it+1 once used;
           // the gathers of tile it + NST (into tile it's slot, free since the
-          // last step) and the softmax of tile it+1 run under these MFMAs
-          // (past the list the softmax sees only masked rows: no effect)
+          // last step) and the softmax stages of tile it+1 sit between these
+          // MFMA groups, so their VALU work overlaps the MFMAs instead of
+          // running before them (past the list the softmax sees only masked
+          // rows: no effect)
           if constexpr (REFILL) dma_prep(it + S::NST);
-          const bf16x8 pb = softmax(it + 1, scn, false);
+          SmState st;
+          sm_init(st);
 #pragma unroll
           for (int f = 0; f < 8; ++f) {
 #pragma unroll
             for (int hf = 0; hf < 4; ++hf)
               o[4 * f + hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vpre[f], pall[hf], o[4 * f + hf], 0, 0, 0);
             vpre[f] = read_vt(it + 1, f);
+            if (f == 0) sm_scale(it + 1, scn, 0, st);
+            if (f == 1) sm_scale(it + 1, scn, 1, st);
+            if (f == 2) sm_reduce(st, false);
+            if (f == 3) sm_exp(0, st);
+            if (f == 4) sm_exp(1, st);
+            if (f == 5) sm_finish(st);
             if constexpr (REFILL) dma_line(f);
+            __builtin_amdgcn_sched_barrier(0);
           }
           if constexpr (REFILL && S::NLINES > 8) dma_line(8);
-          publish(pb, (it + 1) & 1);
+          publish(st.pb, (it + 1) & 1);
         };
         int it = 0;
         if constexpr (S::RSPLIT) {
