@@ -275,6 +275,18 @@ __device__ __forceinline__ int translate(const FwdArgs& a, int j, int seq_ok, in
   return (page << a.page_shift) | (j & ((1 << a.page_shift) - 1));
 }
 
+// LDS word of compacted list entry k: each 64-word block rotated by its block
+// index, so the compaction's writes (a thread stores its survivors at
+// consecutive positions, neighbouring lanes 8 or 16 words apart) spread over
+// the banks; reads of consecutive entries stay consecutive words modulo 64.
+__device__ __forceinline__ int lpos(int k) { return (k & ~63) | ((k + (k >> 6)) & 63); }
+
+// Position of a staged accumulator fragment f of lane (g4, n) in the epilogue
+// staging area: each 16-lane row rotated by f + 8 * (g4 >> 1), so the
+// merge's reads (16 lanes, one head n, fragments c / 2 and lane rows
+// 2 * (c & 1)) hit 16 different bank groups.  A bijection within each row.
+__device__ __forceinline__ int spos(int f, int g4, int n) { return f * 64 + g4 * 16 + ((n + f + 8 * (g4 >> 1)) & 15); }
+
 // 16-bit field g of a packed array (two fields per word), g a runtime value
 __device__ __forceinline__ uint32_t field16(const uint32_t (&w)[8], int g) {
   uint32_t v = 0;
@@ -321,7 +333,7 @@ __device__ __forceinline__ int compact_chunk(const FwdArgs& a, const int (&raw)[
     int pos = base + incl - cnt;
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
-      if (sl[i] >= 0) { list[pos] = sl[i]; ++pos; }
+      if (sl[i] >= 0) { list[lpos(pos)] = sl[i]; ++pos; }
     }
     __syncthreads();
     return n_valid;
@@ -380,7 +392,7 @@ __device__ __forceinline__ int compact_chunk(const FwdArgs& a, const int (&raw)[
   for (int i = 0; i < EPT; ++i) {
     const int g = grp[i];
     if (g >= 0) {
-      list[field16(base, g)] = sl[i];
+      list[lpos((int)field16(base, g))] = sl[i];
       const uint32_t one = 1u << ((g & 1) * 16);
 #pragma unroll
       for (int k = 0; k < 8; ++k) base[k] += ((g >> 1) == k) ? one : 0u;
@@ -623,7 +635,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         const int r = 8 * rh + (lane >> 3);
         int li = tstart + r;
         li = (li < n_valid) ? li : n_valid - 1;           // tail rows repeat the last valid row
-        const int slot = list[li];
+        const int slot = list[lpos(li)];
         const int q = (lane & 7) ^ swz<S::FP8>(r);
         const uint8_t* g = a.kv + row_offset<S::FP8, S::ROWB>(a, slot) + q * 16;
         const uint32_t mb = tl + (uint32_t)rh * 1024u;
@@ -647,7 +659,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
           const int r = hg * SR + lane;
           int li = tstart + r;
           li = (li < n_valid) ? li : n_valid - 1;
-          const int slot = list[li];
+          const int slot = list[lpos(li)];
           const int64_t page = slot >> a.page_shift;
           const int64_t rin = slot & ((1 << a.page_shift) - 1);
           const uint8_t* g = a.kv + page * ((int64_t)(S::ROWB + FP8_SCALE_BYTES) << a.page_shift) +
@@ -928,17 +940,24 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
             for (int blk = 0; blk < 4; ++blk) pb[blk][j] = (__bf16)(pj * sv[j][blk]);
           }
           l_run[0] += psum;
+          // P of block blk from wave f: 8 bytes per lane, contiguous over the
+          // lanes ([stream][block][wave][lane]), so the writes are free of bank
+          // conflicts
 #pragma unroll
           for (int blk = 0; blk < 4; ++blk)
-            *(LDS_AS bf16x4*)(lds + S::PEX_OFF + ((rg * 4 + blk) * 64 + lane) * 16 + f * 8) = pb[blk];
+            *(LDS_AS bf16x4*)(lds + S::PEX_OFF + (((rg * 4 + blk) * 2 + f) * 64 + lane) * 8) = pb[blk];
         }
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         if (active) {
           // B operands of this wave's two blocks: rows 4*g4 + j (fragment 0), 16 + 4*g4 + j (fragment 1)
           bf16x8 pall[2];
 #pragma unroll
-          for (int b2 = 0; b2 < 2; ++b2)
-            pall[b2] = *(const LDS_AS bf16x8*)(lds + S::PEX_OFF + ((rg * 4 + 2 * f + b2) * 64 + lane) * 16);
+          for (int b2 = 0; b2 < 2; ++b2) {
+            const LDS_AS uint8_t* pp = lds + S::PEX_OFF + ((rg * 4 + 2 * f + b2) * 2 * 64 + lane) * 8;
+            const bf16x4 lo = *(const LDS_AS bf16x4*)pp;              // rows 4*g4 + j (wave 0's fragment)
+            const bf16x4 hi = *(const LDS_AS bf16x4*)(pp + 64 * 8);   // rows 16 + 4*g4 + j (wave 1's)
+            pall[b2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
           typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
           i32x2 vw[16];
 #pragma unroll
@@ -983,7 +1002,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
           const int pg = list[li >> a.page_shift];
           slot = ((pg < 0 ? 0 : pg) << a.page_shift) | (li & ((1 << a.page_shift) - 1));
         } else {
-          slot = list[li];
+          slot = list[lpos(li)];
         }
         dg = a.kv + (int64_t)slot * S::ROWB + ((lane & 7) ^ swz<S::FP8>(r)) * 16;
         dmb = tile_lds(itd) + (uint32_t)hg * 1024u;
@@ -1406,11 +1425,11 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
     // the row stream's 32 fragments, staged where its first wave's would be
     f32x4* ost = reinterpret_cast<f32x4*>(smem) + (size_t)(rg * S::HG) * 32 * 64;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ost[(16 * hg + i) * 64 + lane] = o[i];
+    for (int i = 0; i < 16; ++i) ost[spos(16 * hg + i, g4, n)] = o[i];
   } else {
     f32x4* ost = reinterpret_cast<f32x4*>(smem) + (size_t)wave * 32 * 64;
 #pragma unroll
-    for (int f = 0; f < 32; ++f) ost[f * 64 + lane] = o[f];
+    for (int f = 0; f < 32; ++f) ost[spos(f, g4, n)] = o[f];
   }
   // (only shapes without the output-dim split reach here: one query row per
   // work-group, row streams merged through LDS)
@@ -1436,9 +1455,9 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         const float fct = fast_exp2(stat[(w * 16 + nn) * 2] - M);
         L += fct * (stat[(w * 16 + nn) * 2 + 1] + (S::PAIR ? stat[((w + 1) * 16 + nn) * 2 + 1] : 0.f));
         // dims 8c..8c+7 = fragment c/2, lanes (2*(c&1) + {0,1})*16 + nn, j = 0..3
-        const f32x4* ost = reinterpret_cast<const f32x4*>(smem) + (size_t)w * 32 * 64 + (c >> 1) * 64;
-        const f32x4 v0 = ost[(2 * (c & 1) + 0) * 16 + nn];
-        const f32x4 v1 = ost[(2 * (c & 1) + 1) * 16 + nn];
+        const f32x4* ost = reinterpret_cast<const f32x4*>(smem) + (size_t)w * 32 * 64;
+        const f32x4 v0 = ost[spos(c >> 1, 2 * (c & 1) + 0, nn)];
+        const f32x4 v1 = ost[spos(c >> 1, 2 * (c & 1) + 1, nn)];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           acc[j] += fct * v0[j];
