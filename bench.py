@@ -33,6 +33,8 @@ Workloads (synthetic, seeded; `--workload` runs one of them alone):
                        (N(0,1) from a seeded device generator), k = 2048
   indexer_4096x65536   the indexer step: MQA logits (64 heads x 128 dims) of 4096 rows against
                        their causal 65536-key history, then top-k 2048
+  plan_sweep           native vs padded head tiles and automatic vs no KV splits at T = 16..512,
+                       h = 8 / 16 / 32 (the dispatch plan's crossovers)
 """
 from __future__ import annotations
 
@@ -473,6 +475,54 @@ def bench_indexer(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_plan_sweep(args):
+    """The dispatch plan's choices at small batches (native head tiles vs
+    padding to 64 heads, automatic KV splits vs none): T decode rows spread
+    over the c2_decode pool (32 sequences x 16384 tokens, top-k 2048), h in
+    {8, 16, 32}.  Prints one JSON line with the step time of every variant."""
+    import torch
+    from sparse_mla_attention_04_amd import binding as B
+    from sparse_mla_attention_04_amd import inputs as G
+    from sparse_mla_attention_04_amd.inputs import DeviceCase as Dev
+    rows = []
+    for T in (16, 32, 64, 128, 256, 512):
+        nseq = min(T, 32)
+        per = T // nseq
+        case = G.build_case("plan_sweep_T%d" % T, seed=1009, hist=[16384 - per] * nseq, new=[per] * nseq,
+                            num_heads=32, topk=2048)
+        dev = Dev(case)
+        for h in (8, 16, 32):
+            q = dev.q[:, :h, :]
+            out = torch.empty((T, h, 512), dtype=torch.bfloat16, device="cuda")
+            lse = torch.empty((T, h), dtype=torch.float32, device="cuda")
+            for tiling, splits in (("native", 0), ("pad64", 0), ("native", 1), ("pad64", 1)):
+                p = B.params_for(q, dev.kv, dev.idx, out, lse, topk=case.topk, scale=case.scale,
+                                 block_table=dev.bt, token_seq=dev.ts, tiling=tiling, num_splits=splits)
+                pl = B.plan(p)
+                ws = B.workspace_for(p, "cuda")
+                step = lambda: B.fwd(q, dev.kv, dev.idx, out, lse, topk=case.topk, scale=case.scale, workspace=ws,
+                                     block_table=dev.bt, token_seq=dev.ts, params=p)
+                for _ in range(args.warmup):
+                    step()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(args.steps):
+                    step()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) / args.steps * 1e3
+                rows.append({"T": T, "h": h, "tiling": tiling, "splits_requested": splits or "auto",
+                             "num_splits": pl.num_splits, "kernel_variant": pl.kernel_variant, "us_per_step": round(us, 2)})
+                print("plan sweep T=%d h=%d %s splits=%s -> S=%d v%d %.2f us" % (
+                    T, h, tiling, splits or "auto", pl.num_splits, pl.kernel_variant, us), file=sys.stderr, flush=True)
+        del dev
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "sparse MLA fwd: plan sweep, us per step", "unit": "us", "steps": args.steps,
+                      "warmup": args.warmup, "config": {"workload": "plan_sweep", "pool": "32 x 16384 tokens",
+                                                         "topk": 2048}, "rows": rows}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -492,6 +542,8 @@ def main():
         return bench_topk(args)
     if args.workload == "indexer_4096x65536":
         return bench_indexer(args)
+    if args.workload == "plan_sweep":
+        return bench_plan_sweep(args)
 
     headline = args.workload == "headline"
     main_name = "c5_fp8" if headline else args.workload

@@ -82,6 +82,13 @@ int splits_for(const smla_params* p, int32_t num_cus, const smla::FwdShape& sh) 
   const int64_t T = p->num_tokens;
   if (T <= 0 || T >= num_cus) return 1;
   int64_t s = num_cus / T;
+  // one head group: a row streams its gathers at ~50 GB/s per work-group, so
+  // from #CU / 4 rows on the unsplit batch already draws most of the gather
+  // bandwidth and the merge launch costs more than splitting gains (MI355X,
+  // rows of 2048 entries over a 604 MB pool: T = 128 at h = 8 ran 51.8 us
+  // unsplit, 54.7 us in two splits; T = 64 ran 34.9 us in four splits, 42.2
+  // unsplit; at h = 32, T = 128 still gains from two splits, 59.7 vs 75.8 us)
+  if (sh.head_groups == 1 && s < 4) return 1;
   // keep at least one tile per row group in every split; with one head
   // group, at least 256 list entries (a split's fixed start-up and merge cost
   // outweighs a shorter share: T = 64 rows of 128 entries at h = 8 ran

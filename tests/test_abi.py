@@ -205,6 +205,10 @@ def test_plan_for_is_pure_and_splits_small_batches():
     assert B.plan(_params(num_tokens=4096, topk=2048, num_heads=32, kv_format="fp8"), num_cus=256).kernel_variant == 0
     pn = B.plan(_params(num_tokens=4096, topk=2048, num_heads=8, geometry="nope"), num_cus=256)
     assert pn.kernel_variant == 2 and pn.lds_bytes <= 80 * 1024
+    # one head group: no split below four per row (T >= #CU / 4); two head groups still split
+    assert B.plan(_params(num_tokens=128, topk=2048, num_heads=8), num_cus=256).num_splits == 1
+    assert B.plan(_params(num_tokens=64, topk=2048, num_heads=8), num_cus=256).num_splits == 4
+    assert B.plan(_params(num_tokens=128, topk=2048, num_heads=32), num_cus=256).num_splits == 2
     # one head group: every split keeps at least 256 list entries
     assert B.plan(_params(num_tokens=64, topk=128, num_heads=8), num_cus=256).num_splits == 1
     assert B.plan(_params(num_tokens=64, topk=512, num_heads=8), num_cus=256).num_splits == 2
