@@ -267,7 +267,8 @@ int run(Mode mode, const smla_params* p, const void* q, const void* kv_cache, co
   a.max_blocks = p->max_blocks_per_seq;
   a.grid_per_xcd = (int32_t)(pl.grid / 8);
   a.write_partials = partials ? 1 : 0;
-  a.scale_log2 = p->softmax_scale * 1.44269504088896340736f;
+  a.scale_log2 = std::fabs(p->softmax_scale) * 1.44269504088896340736f;
+  a.q_neg = p->softmax_scale < 0.f;
   // slot order: 16 ranges of physical row (the top 4 bits of the row number)
   a.bucket_shift = pl.gather_order == SMLA_GATHER_SLOT ? bucket_shift_for(a.num_slots) : -1;
 
@@ -394,7 +395,8 @@ int sparse_mla_dense_fwd(const smla_params* p, const void* q, const void* kv_cac
   a.max_blocks = p->max_blocks_per_seq;
   a.grid_per_xcd = (int32_t)((units + 7) / 8);
   a.write_partials = 0;
-  a.scale_log2 = p->softmax_scale * 1.44269504088896340736f;
+  a.scale_log2 = std::fabs(p->softmax_scale) * 1.44269504088896340736f;
+  a.q_neg = p->softmax_scale < 0.f;
   a.bucket_shift = -1;
   a.query_start = query_start;
   a.positions = positions;

@@ -564,6 +564,14 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
 #pragma unroll
       for (int kk = 0; kk < S::KS; ++kk) qb[18 * e + kk] = bf16x8{};
     }
+    // a negative softmax scale: the kernels scale by |scale| and take -q
+    // (negating a bf16 value is exact), so the scaled scores are unchanged and
+    // the softmax code may assume a non-negative scale
+    if (a.q_neg) {
+#pragma unroll
+      for (int kk = 0; kk < S::KS; ++kk)
+        qb[18 * e + kk] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, qb[18 * e + kk]) ^ 0x80008000u);
+    }
   }
 
   // the row's sequence (LOGICAL mode) is requested after the index entries and
@@ -1045,7 +1053,19 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         st.mx[0] = st.mx[1] = NEG_INF;
         st.psum[0] = st.psum[1] = 0.f;
       };
-      auto sm_scale = [&](int it, const f32x4* scv, int q, SmState& st) {
+      // MASK false (a whole tile: every row is listed): the raw scores are
+      // kept, their maximum is scaled once (the scale is non-negative), and the
+      // exponent is one fma; MASK true: rows past the list are -inf.
+      auto sm_scale = [&](int it, const f32x4* scv, int q, SmState& st, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        if constexpr (!MASK) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            st.x[q][j] = scv[q][j];
+            st.mx[S::RSPLIT ? q : 0] = fmaxf(st.mx[S::RSPLIT ? q : 0], scv[q][j]);
+          }
+          return;
+        }
         const int left = n_valid - it * S::RT;
         // dense mode: positions past the slot's own row, or on an invalid
         // page (pages hold >= 16 rows, so a 16-row fragment has one page)
@@ -1063,9 +1083,13 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
           st.mx[S::RSPLIT ? q : 0] = fmaxf(st.mx[S::RSPLIT ? q : 0], st.x[q][j]);
         }
       };
-      auto sm_reduce = [&](SmState& st, bool first) {
+      auto sm_reduce = [&](SmState& st, bool first, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-        for (int e = 0; e < S::NE; ++e) st.mx[e] = max_xor16_32(st.mx[e]);
+        for (int e = 0; e < S::NE; ++e) {
+          st.mx[e] = max_xor16_32(st.mx[e]);
+          if constexpr (!MASK) st.mx[e] *= a.scale_log2;
+        }
         if constexpr (S::RSPLIT) {
           if (first) {
             // in exchange buffer 1: buffer 0 receives P of this tile right after
@@ -1088,10 +1112,12 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
           overflow |= (st.mx[e] > m_run[e] + REF_HEADROOM);
         }
       };
-      auto sm_exp = [&](int q, SmState& st) {
+      auto sm_exp = [&](int q, SmState& st, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          float pj = fast_exp2(st.x[q][j] - m_run[S::RSPLIT ? q : 0]);
+          float pj = MASK ? fast_exp2(st.x[q][j] - m_run[S::RSPLIT ? q : 0])
+                          : fast_exp2(__builtin_fmaf(st.x[q][j], a.scale_log2, -m_run[S::RSPLIT ? q : 0]));
           // dense mode: a slot may see no valid position yet (reference unset)
           if constexpr (S::DENSE) pj = (m_run[0] == NEG_INF) ? 0.f : pj;
           st.psum[S::RSPLIT ? q : 0] += pj;
@@ -1112,11 +1138,11 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
       auto softmax = [&](int it, const f32x4* scv, bool first) -> bf16x8 {
         SmState st;
         sm_init(st);
-        sm_scale(it, scv, 0, st);
-        sm_scale(it, scv, 1, st);
-        sm_reduce(st, first);
-        sm_exp(0, st);
-        sm_exp(1, st);
+        sm_scale(it, scv, 0, st, std::true_type{});
+        sm_scale(it, scv, 1, st, std::true_type{});
+        sm_reduce(st, first, std::true_type{});
+        sm_exp(0, st, std::true_type{});
+        sm_exp(1, st, std::true_type{});
         sm_finish(st);
         return st.pb;
       };
@@ -1237,15 +1263,17 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
           // every wave's reads of tile it (its V^T operands) have completed
           // before any gather refills that slot, and P of tile it is published
           asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-          bf16x8 pall[4];
-#pragma unroll
-          for (int hf = 0; hf < 4; ++hf) pall[hf] = pex[(it & 1) * 256 + hf * 64 + lane];
           f32x4 scn[2];
           if (it + 1 < nit) {
             scores(it + 1, scn);
           } else {
             scn[0] = scn[1] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
+          // P of tile it, read after the score phase: read before it, these four
+          // reads took slots of the K operand ring's first group of reads
+          bf16x8 pall[4];
+#pragma unroll
+          for (int hf = 0; hf < 4; ++hf) pall[hf] = pex[(it & 1) * 256 + hf * 64 + lane];
           // P.V of tile it over this wave's 8 output fragments x 4 head groups;
           // each fragment's V^T registers are refilled from tile it+1 once used;
           // the gathers of tile it + NST (into tile it's slot, free since the
@@ -1262,11 +1290,14 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
             for (int hf = 0; hf < 4; ++hf)
               o[4 * f + hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vpre[f], pall[hf], o[4 * f + hf], 0, 0, 0);
             vpre[f] = read_vt(it + 1, f);
-            if (f == 0) sm_scale(it + 1, scn, 0, st);
-            if (f == 1) sm_scale(it + 1, scn, 1, st);
-            if (f == 2) sm_reduce(st, false);
-            if (f == 3) sm_exp(0, st);
-            if (f == 4) sm_exp(1, st);
+            // tiles before the last NST are whole (only the last listed tile
+            // can be partial): no masking in the refill steps
+            using MT = std::integral_constant<bool, !REFILL || S::RSPLIT || S::DENSE>;
+            if (f == 0) sm_scale(it + 1, scn, 0, st, MT{});
+            if (f == 1) sm_scale(it + 1, scn, 1, st, MT{});
+            if (f == 2) sm_reduce(st, false, MT{});
+            if (f == 3) sm_exp(0, st, MT{});
+            if (f == 4) sm_exp(1, st, MT{});
             if (f == 5) sm_finish(st);
             if constexpr (REFILL) dma_line(f);
             __builtin_amdgcn_sched_barrier(0);

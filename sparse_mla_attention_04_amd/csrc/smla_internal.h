@@ -39,7 +39,9 @@ struct FwdArgs {
   int32_t page_shift, index_mode, num_seqs, max_blocks;
   int32_t grid_per_xcd;       // launched work-groups / 8
   int32_t write_partials;     // 1: write fp32 partials to ws_out / ws_lse instead of out / lse
-  float scale_log2;           // softmax_scale * log2(e)
+  float scale_log2;           // |softmax_scale| * log2(e) (never negative)
+  int32_t q_neg;              // softmax_scale < 0: queries enter with their sign flipped, so
+                              // every score is |scale| * (-q) . k = scale * q . k exactly
   int32_t bucket_shift;       // >= 0: gather each row's entries grouped by (slot >> shift), 16 groups; -1: list order
   // dense causal mode only
   const int32_t* query_start; // int32 [num_seqs + 1]: rows of sequence s are [query_start[s], query_start[s+1])

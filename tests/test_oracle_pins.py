@@ -167,6 +167,29 @@ def test_repeated_index_returns_that_row(k):
         np.testing.assert_allclose(lse[t], qk * c.scale + math.log(k), rtol=1e-13, atol=1e-12)
 
 
+def test_zero_and_negative_scale_closed_forms():
+    """scale 0: every listed row weighs the same, so out is the plain mean of
+    the listed value rows (a multiset) and lse = ln n; scale -c equals scale c
+    applied to -q (the score c * (-q) . k is the same number)."""
+    c = G.make_mini(seed=15, num_heads=4, topk=40, num_seqs=1, tokens_per_seq=3, drop_frac=0.2)
+    out0, lse0 = O.sparse_mla_forward(c.q, c.kv, c.topk_idx, topk=c.topk, scale=0.0,
+                                      block_table=c.block_table, token_seq=c.token_seq)
+    flat = O.bf16_to_float(c.kv.reshape(-1, O.D_QK))
+    P = c.page_size
+    for t in range(c.num_tokens):
+        ent = [int(j) for j in c.topk_idx[t, :c.topk] if j >= 0]
+        rows = [int(c.block_table[c.token_seq[t], j // P]) * P + j % P for j in ent]
+        mean = flat[rows, :512].mean(axis=0)
+        np.testing.assert_allclose(out0[t], np.broadcast_to(mean, out0[t].shape), rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(lse0[t], math.log(len(rows)), rtol=1e-14)
+    neg_q = (c.q ^ np.uint16(0x8000)).astype(np.uint16)
+    a = O.sparse_mla_forward(c.q, c.kv, c.topk_idx, topk=c.topk, scale=-c.scale,
+                             block_table=c.block_table, token_seq=c.token_seq)
+    b = O.sparse_mla_forward(neg_q, c.kv, c.topk_idx, topk=c.topk, scale=c.scale,
+                             block_table=c.block_table, token_seq=c.token_seq)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
 def test_one_and_two_rows_closed_form():
     c = G.make_mini(seed=14, num_heads=3, topk=8, num_seqs=1, tokens_per_seq=2)
     flat = O.bf16_to_float(c.kv.reshape(-1, O.D_QK))

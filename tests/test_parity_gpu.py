@@ -169,6 +169,36 @@ def test_large_score_spread_recomputes_exactly(splits, h, variant):
     check(out, lse, ro, rl, "score spread")
 
 
+@pytest.mark.parametrize("mul", [-1.0, 0.0, 2.5])
+@pytest.mark.parametrize("h,kv_format,rope,variant,splits", [
+    (8, "bf16", 64, 0, 1), (8, "bf16", 64, 2, 1), (8, "bf16", 64, 0, 3), (32, "bf16", 64, 2, 1),
+    (64, "bf16", 64, 0, 1), (64, "bf16", 64, 0, 2), (64, "bf16", 64, 2, 1), (64, "bf16", 0, 0, 1),
+    (8, "fp8", 64, 0, 1), (8, "fp8", 64, 2, 2), (16, "fp8", 0, 0, 1)])
+def test_negative_zero_and_large_scale(mul, h, kv_format, rope, variant, splits):
+    """softmax_scale = -c, 0 and 2.5c (c = 1/sqrt(d)) on every kernel family:
+    the kernels scale by |scale| and flip the queries' sign for a negative
+    one, and a zero scale weighs every listed row the same."""
+    say("scale x%g" % mul, h, kv_format, rope, variant, splits)
+    c = G.make_mini(seed=43, num_heads=h, topk=300, kv_format=kv_format, rope_dims=rope, drop_frac=0.2)
+    c = G.Case(**{**c.__dict__, "scale": float(np.float32(c.scale * mul))})
+    out, lse = to_np(*run_gpu(Dev(c), num_splits=splits, variant=variant))
+    check(out, lse, *oracle(c), what="scale x%g h=%d %s rope %d v%d s%d" % (mul, h, kv_format, rope, variant, splits))
+
+
+@pytest.mark.parametrize("mul", [-1.0, 0.0])
+def test_dense_negative_and_zero_scale(mul):
+    """The dense causal entry with softmax_scale = -c and 0."""
+    say("dense scale x%g" % mul)
+    c = G.build_case("dense", seed=84, hist=[0, 100, 300], new=[20, 9, 40], num_heads=8, topk=8)
+    c = G.Case(**{**c.__dict__, "scale": float(np.float32(c.scale * mul))})
+    qs, pos, idx = _dense_inputs(c)
+    out, lse = _run_dense(c, qs, pos)
+    from oracle import sparse_mla_oracle as O
+    ro, rl = O.sparse_mla_forward(c.q, c.kv, idx, topk=idx.shape[1], scale=c.scale, index_mode="logical",
+                                  block_table=c.block_table, token_seq=c.token_seq)
+    check(out, lse, ro, rl, "dense scale x%g" % mul)
+
+
 def test_empty_and_out_of_range_rows():
     say("empty rows")
     c = G.make_mini(seed=28, num_heads=8, topk=100)
