@@ -5,14 +5,24 @@
 // order inside a row is not defined).
 //
 // One work-group (four waves) per query row.  The k-th largest score is found
-// by a radix select over an order-preserving 32-bit key: an LDS histogram of
-// the key's top 11 bits over the whole row names the bucket holding the k-th
-// key.  When that bucket fits in LDS, a second read of the row writes every
-// key above the bucket and copies the bucket's keys to LDS, where the
-// remaining 11 + 10 bits are resolved and ties are cut by index (two reads of
-// the row in all).  A larger bucket (heavily tied rows) takes two more
-// histogram rounds over the row and a final pass that writes the keys above
-// the k-th key and the lowest-index keys equal to it.
+// by a radix select over an order-preserving 32-bit key.
+//   One read (long rows): every 32nd 128-byte line of the row is read as a
+//   sample, and the sample's r-th largest key tau is found in LDS, r chosen
+//   so that about (k + CAP) / 2 keys of the row are expected at or above it.
+//   One pass over the row then copies every key >= tau (and its index) to
+//   LDS.  When k <= that count <= CAP, the candidates hold the whole top-k and
+//   every key equal to the k-th, and the selection finishes in LDS.  Any
+//   other count (an unrepresentative sample) takes the two-read route below.
+//   Measured on MI355X (4096 rows x 65536 N(0,1) scores, k = 2048): 0.476 ms
+//   with two reads, 0.474 ms with one read while each wave kept one load in
+//   flight, 0.339 ms with one read in batches of eight loads per thread.
+//   Two reads: an LDS histogram of the key's top 11 bits over the whole row
+//   names the bucket holding the k-th key.  When that bucket fits in LDS, a
+//   second read of the row writes every key above the bucket and copies the
+//   bucket's keys to LDS, where the remaining 11 + 10 bits are resolved and
+//   ties are cut by index.  A larger bucket (heavily tied rows) takes two
+//   more histogram rounds over the row and a final pass that writes the keys
+//   above the k-th key and the lowest-index keys equal to it.
 #include "smla_internal.h"
 
 namespace smla {
@@ -36,13 +46,16 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 constexpr int NB = 2048;                 // bins of the widest digit
 constexpr int SHIFTS[3] = {21, 10, 0};
 constexpr int WIDTHS[3] = {11, 11, 10};
-// Keys of the top-digit bucket held in LDS (N(0,1) scores, 65536 keys,
-// k = 2048: about 1200).  24 KB of LDS per work-group lets six run on a CU;
-// measured on MI355X (4096 x 65536, k = 2048): 0.52 ms with room for 3072
-// keys, 0.47 ms for 2048 or 1536, 0.82 ms for 1024 (the bucket no longer
-// fits and rows take the four-read path); histogram copies against LDS
-// atomic collisions and deeper load unrolling did not help.
-constexpr int CAP = 2048;
+// Candidate keys (and indices) held in LDS: the one-read route's keys >= tau
+// (about 3072 for k = 2048), or the two-read route's top-digit bucket (about
+// 1200 for N(0,1) scores, 65536 keys, k = 2048).
+constexpr int CAP = 4096;
+// One-read route: sampled lines are every LSTRIDE-th 128-byte line, at most
+// CAP sample keys, and the sample rank r behind tau at least MIN_RANK (the
+// count of row keys >= tau then has a relative spread of at most about
+// 1 / sqrt(MIN_RANK)).
+constexpr int LSTRIDE = 32;
+constexpr int MIN_RANK = 48;
 
 // Radix step on a filled histogram of nb bins: the bin in which the count of
 // keys, taken from the top bin down, reaches kr.  Thread j owns bins
@@ -133,6 +146,160 @@ __global__ void __launch_bounds__(256) smla_topk_kernel(TopkArgs a) {
     mask |= (uint32_t)(nb - 1) << shift;
     kr = ctl[1];
   };
+  // radix select over the nc LDS candidates: with (prefix, mask, kr) on entry
+  // describing the keys still open, leaves prefix = the kr-th largest key,
+  // kr = how many keys equal to it are taken, ctl[4] = how many there are
+  auto lds_select = [&](int nc, int first_pass) {
+    for (int pass = first_pass; pass < 3; ++pass) {
+      const int shift = SHIFTS[pass];
+      const int nb = 1 << WIDTHS[pass];
+      for (int i = tid; i < nb; i += 256) hist[i] = 0u;
+      __syncthreads();
+      for (int c = tid; c < nc; c += 256) {
+        const uint32_t u = cand_key[c];
+        if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & (uint32_t)(nb - 1)], 1u);
+      }
+      __syncthreads();
+      find_bin(hist, nb, kr, ctl, wsum, tid, lane, wave);
+      prefix |= (uint32_t)ctl[0] << shift;
+      mask |= (uint32_t)(nb - 1) << shift;
+      kr = ctl[1];
+    }
+  };
+  // writes the selection from the nc LDS candidates, which hold every key
+  // >= prefix (the k-th largest key); keys above it were already written to
+  // out[0 .. n_out) when n_out > 0.  kr of the ctl[4] keys equal to prefix
+  // are taken, the lowest-index ones.
+  auto write_selection = [&](int nc, int n_out) {
+    const int n_eq = ctl[4];
+    uint32_t vsel = 0u;   // ties are taken while ~index >= vsel
+    if (n_eq > kr) {
+      // radix select of the kr-th largest ~index among the ties (indices are
+      // distinct, so exactly kr ties reach it)
+      uint32_t vpre = 0u, vmask = 0u;
+      int kv = kr;
+#pragma unroll
+      for (int pass = 0; pass < 3; ++pass) {
+        const int shift = SHIFTS[pass];
+        const int nb = 1 << WIDTHS[pass];
+        __syncthreads();
+        for (int i = tid; i < nb; i += 256) hist[i] = 0u;
+        __syncthreads();
+        for (int c = tid; c < nc; c += 256) {
+          const uint32_t v = ~(uint32_t)cand_idx[c];
+          if (cand_key[c] == prefix && (v & vmask) == vpre) atomicAdd(&hist[(v >> shift) & (uint32_t)(nb - 1)], 1u);
+        }
+        __syncthreads();
+        find_bin(hist, nb, kv, ctl, wsum, tid, lane, wave);
+        vpre |= (uint32_t)ctl[0] << shift;
+        vmask |= (uint32_t)(nb - 1) << shift;
+        kv = ctl[1];
+      }
+      vsel = vpre;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      ctl[2] = n_out;
+      ctl[3] = 0;
+    }
+    __syncthreads();
+    for (int c = tid; c < nc; c += 256) {
+      const uint32_t u = cand_key[c];
+      if (u > prefix) {
+        out[atomicAdd(&ctl[2], 1)] = cand_idx[c];
+      } else if (u == prefix && ~(uint32_t)cand_idx[c] >= vsel) {
+        out[(k - kr) + atomicAdd(&ctl[3], 1)] = cand_idx[c];
+      }
+    }
+  };
+
+  // ---- one read: a sampled threshold, then one pass collecting keys >= tau
+  if (vec && k <= CAP / 2) {
+    const int lines = len >> 5;                       // whole 128-byte lines of the row
+    const int nsl_all = lines / LSTRIDE;              // sampled lines
+    const int nsl = nsl_all < CAP / 32 ? nsl_all : CAP / 32;
+    const int ns = nsl * 32;                          // sample keys
+    const int64_t rank = ((int64_t)(k + CAP) / 2 * ns + len / 2) / len;
+    if (nsl > 0 && rank >= MIN_RANK && rank <= ns) {
+      // sample line m is line m * (lines / nsl): thread j of the 8 per line
+      // reads 16 bytes of it
+      const f32x4* row4 = reinterpret_cast<const f32x4*>(row);
+      const int lstep = lines / nsl;
+      for (int j = tid; j < nsl * 8; j += 256) {
+        const int m = j >> 3;
+        const f32x4 v = row4[(int64_t)m * lstep * 8 + (j & 7)];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cand_key[4 * j + q] = order_key(v[q]);
+      }
+      __syncthreads();
+      kr = (int)rank;
+      lds_select(ns, 0);
+      const uint32_t tau = prefix;                    // the sample's rank-th largest key
+      // one pass: every key >= tau to LDS, one LDS atomic per wave and
+      // sixteen scores (wave-aggregated appends in index order within a lane)
+      __syncthreads();
+      if (tid == 0) ctl[3] = 0;
+      __syncthreads();
+      const int n4 = len >> 2;
+      auto append = [&](uint32_t u, int i, bool ok) {
+        if (ok && u >= tau) {
+          const int c = atomicAdd(&ctl[3], 1);
+          if (c < CAP) {
+            cand_key[c] = u;
+            cand_idx[c] = i;
+          }
+        }
+      };
+      // batches of U 16-byte loads per thread, all issued before any key of
+      // the batch is examined (the appends branch, which would otherwise
+      // leave one load in flight per wave), the next batch requested before
+      // the current one is examined
+      constexpr int U = 8;
+      f32x4 cur[U], nxt[U];
+      auto load_batch = [&](int j0, f32x4 (&v)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int j = j0 + u * 256 + tid;
+          v[u] = row4[j < n4 ? j : n4 - 1];
+        }
+      };
+      if (n4 > 0) load_batch(0, cur);
+      for (int j0 = 0; j0 < n4; j0 += 256 * U) {
+        if (j0 + 256 * U < n4) load_batch(j0 + 256 * U, nxt);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int j = j0 + u * 256 + tid;
+          const bool ok = j < n4;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) append(order_key(cur[u][q]), 4 * j + q, ok);
+        }
+        if (j0 + 256 * U < n4) {
+#pragma unroll
+          for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+        }
+      }
+      for (int i0 = n4 << 2; i0 < len; i0 += 256) {
+        const int i = i0 + tid;
+        append(i < len ? order_key(row[i]) : 0u, i, i < len);
+      }
+      __syncthreads();
+      const int nc = ctl[3];
+      if (nc >= k && nc <= CAP) {
+        prefix = 0u;
+        mask = 0u;
+        kr = k;
+        lds_select(nc, 0);
+        write_selection(nc, 0);
+        return;
+      }
+      // an unrepresentative sample: start over on the two-read route
+      prefix = 0u;
+      mask = 0u;
+      kr = k;
+      __syncthreads();
+    }
+  }
+
   // invariant: at least kr of the keys matching (prefix, mask) remain, and
   // the keys above that bucket (k - kr of them) are all selected
   hist_pass(SHIFTS[0], 1 << WIDTHS[0]);
@@ -174,62 +341,11 @@ __global__ void __launch_bounds__(256) smla_topk_kernel(TopkArgs a) {
     for (int i = done + tid; i < len; i += 256) route(row[i], i);
     __syncthreads();
     const int nc = ctl[3];   // == nbucket
+    const int n_out = ctl[2];
     // ---- the remaining digits over the LDS copy of the bucket
-#pragma unroll
-    for (int pass = 1; pass < 3; ++pass) {
-      const int shift = SHIFTS[pass];
-      const int nb = 1 << WIDTHS[pass];
-      for (int i = tid; i < nb; i += 256) hist[i] = 0u;
-      __syncthreads();
-      for (int c = tid; c < nc; c += 256) {
-        const uint32_t u = cand_key[c];
-        if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & (uint32_t)(nb - 1)], 1u);
-      }
-      __syncthreads();
-      find_bin(hist, nb, kr, ctl, wsum, tid, lane, wave);
-      prefix |= (uint32_t)ctl[0] << shift;
-      mask |= (uint32_t)(nb - 1) << shift;
-      kr = ctl[1];
-    }
-    // prefix is the k-th largest key; kr of the n_eq keys equal to it are
-    // taken, the kr lowest-index ones
-    const int n_eq = ctl[4];
-    uint32_t vsel = 0u;   // ties are taken while ~index >= vsel
-    if (n_eq > kr) {
-      // radix select of the kr-th largest ~index among the ties (indices are
-      // distinct, so exactly kr ties reach it)
-      uint32_t vpre = 0u, vmask = 0u;
-      int kv = kr;
-#pragma unroll
-      for (int pass = 0; pass < 3; ++pass) {
-        const int shift = SHIFTS[pass];
-        const int nb = 1 << WIDTHS[pass];
-        __syncthreads();
-        for (int i = tid; i < nb; i += 256) hist[i] = 0u;
-        __syncthreads();
-        for (int c = tid; c < nc; c += 256) {
-          const uint32_t v = ~(uint32_t)cand_idx[c];
-          if (cand_key[c] == prefix && (v & vmask) == vpre) atomicAdd(&hist[(v >> shift) & (uint32_t)(nb - 1)], 1u);
-        }
-        __syncthreads();
-        find_bin(hist, nb, kv, ctl, wsum, tid, lane, wave);
-        vpre |= (uint32_t)ctl[0] << shift;
-        vmask |= (uint32_t)(nb - 1) << shift;
-        kv = ctl[1];
-      }
-      vsel = vpre;
-    }
-    __syncthreads();
-    if (tid == 0) ctl[3] = 0;
-    __syncthreads();
-    for (int c = tid; c < nc; c += 256) {
-      const uint32_t u = cand_key[c];
-      if (u > prefix) {
-        out[atomicAdd(&ctl[2], 1)] = cand_idx[c];
-      } else if (u == prefix && ~(uint32_t)cand_idx[c] >= vsel) {
-        out[(k - kr) + atomicAdd(&ctl[3], 1)] = cand_idx[c];
-      }
-    }
+    lds_select(nc, 1);
+    // prefix is the k-th largest key; kr of the keys equal to it are taken
+    write_selection(nc, n_out);
     return;
   }
   hist_pass(SHIFTS[1], 1 << WIDTHS[1]);

@@ -89,3 +89,24 @@ def test_topk_rows_longer_than_65536_keys():
     s = rng.standard_normal((6, 70004)).astype(np.float32)
     s[1, :40000] = 0.5                     # a tied threshold bucket larger than the LDS copy
     _check(s, [70004, 65537, 70000, 3000, 0, 69999], 2048)
+
+
+def test_topk_unrepresentative_samples_fall_back():
+    """Long rows whose sampled lines (every 32nd 128-byte line) mislead the
+    one-read route's threshold: sampled lines far above the rest (too few keys
+    reach the threshold) or far below it (too many), and a row whose top keys
+    all sit outside the sampled lines.  Every route must select the same set
+    as the oracle."""
+    say("topk misleading samples")
+    rng = np.random.default_rng(8)
+    T, N = 6, 65536
+    s = rng.standard_normal((T, N)).astype(np.float32)
+    sampled = np.zeros(N, bool)
+    for m in range(0, N // 32, 32):                # sampled lines: 32 scores each
+        sampled[32 * m:32 * m + 32] = True
+    s[0, sampled] = 10.0 + rng.random(int(sampled.sum())).astype(np.float32)
+    s[1, sampled] = -10.0 - rng.random(int(sampled.sum())).astype(np.float32)
+    s[2, ~sampled] += 3.0                          # the top keys avoid the sample
+    s[3, sampled] = 10.0                           # a tied sample
+    _check(s, None, 2048)
+    _check(s, [N, N - 1, 40000, N - 3, 33000, 20000], 2048)
