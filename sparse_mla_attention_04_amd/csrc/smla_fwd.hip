@@ -263,16 +263,38 @@ __device__ __forceinline__ int swz(int r) {
   else return r & 7;
 }
 
-// Translate one index entry to a physical cache row; -1 when skipped.
-__device__ __forceinline__ int translate(const FwdArgs& a, int j, int seq_ok, int64_t bt_row) {
-  if (j < 0) return -1;
-  if (a.index_mode == 0) return (j < a.num_slots) ? j : -1;
-  if (!seq_ok) return -1;
-  const int blk = j >> a.page_shift;
-  if (blk >= a.max_blocks) return -1;
-  const int page = a.block_table[bt_row + blk];
-  if (page < 0 || page >= a.num_pages) return -1;
-  return (page << a.page_shift) | (j & ((1 << a.page_shift) - 1));
+// Translate a thread's EPT index entries to physical cache rows (-1 when
+// skipped).  LOGICAL mode requests every entry's block-table word before
+// using any of them, so the thread waits for one round trip, not EPT: a
+// skipped entry reads the row's first word instead (block tables hold at
+// least one sequence of at least one block), and its result is discarded.
+template <int EPT>
+__device__ __forceinline__ void translate_all(const FwdArgs& a, const int (&raw)[EPT], int seq_ok, int64_t bt_row,
+                                              int (&sl)[EPT]) {
+  if (a.index_mode == 0) {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) sl[i] = (raw[i] >= 0 && raw[i] < a.num_slots) ? raw[i] : -1;
+    return;
+  }
+  bool ok[EPT];
+  int pg[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int blk = raw[i] >> a.page_shift;
+    ok[i] = seq_ok && raw[i] >= 0 && blk < a.max_blocks;
+    pg[i] = a.block_table[bt_row + (ok[i] ? blk : 0)];
+  }
+  // every looked-up word is waited for here, unconditionally: waits the
+  // compiler would otherwise place on the later, lane-dependent uses leave
+  // it counting these loads as pending into the tile loop, where its waits
+  // would also drain the gathers
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) asm volatile("" : : "v"(pg[i]));
+#pragma unroll
+  for (int i = 0; i < EPT; ++i)
+    sl[i] = (ok[i] && pg[i] >= 0 && pg[i] < a.num_pages)
+                ? (pg[i] << a.page_shift) | (raw[i] & ((1 << a.page_shift) - 1))
+                : -1;
 }
 
 // LDS word of compacted list entry k: each 64-word block rotated by its block
@@ -307,13 +329,10 @@ template <int NW, int EPT>
 __device__ __forceinline__ int compact_chunk(const FwdArgs& a, const int (&raw)[EPT], int seq_ok, int64_t bt_row,
                                              int* list, int* wcnt, int wave, int lane) {
   int sl[EPT];
+  translate_all<EPT>(a, raw, seq_ok, bt_row, sl);
   int cnt = 0;
 #pragma unroll
-  for (int i = 0; i < EPT; ++i) {
-    const int s = translate(a, raw[i], seq_ok, bt_row);
-    sl[i] = s;
-    cnt += (s >= 0);
-  }
+  for (int i = 0; i < EPT; ++i) cnt += (sl[i] >= 0);
   if (a.bucket_shift < 0) {
     int incl = cnt;
 #pragma unroll
