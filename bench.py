@@ -109,13 +109,14 @@ def algorithmic_counts(case):
     return int(valid.sum())
 
 
-def counted_traffic(workload_name):
-    """HBM bytes per launch of the attention kernel from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE runs (copy-calibrated), or None when no
-    counters exist for this workload or the kernel source changed since."""
+def counted_traffic(workload_name, source="smla_fwd.hip", kernel="smla_fwd<"):
+    """HBM bytes per launch of the workload's dominant kernel (name containing
+    `kernel`) from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+    (copy-calibrated), or None when no counters exist for this workload or the
+    kernel's source file changed since."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "hbm_traffic_%s.json" % workload_name)
-    src = os.path.join(ROOT, "sparse_mla_attention_04_amd", "csrc", "smla_fwd.hip")
+    src = os.path.join(ROOT, "sparse_mla_attention_04_amd", "csrc", source)
     if not os.path.exists(path):
         return None, None
     with open(path) as f:
@@ -124,7 +125,7 @@ def counted_traffic(workload_name):
         if hashlib.sha256(f.read()).hexdigest() != rec.get("kernel_source_sha256"):
             return None, "stale: kernel source changed since %s" % rec.get("commit")
     for name, v in rec["kernels"].items():
-        if "smla_fwd<" in name:
+        if kernel in name:
             return v["fetch_bytes"] + v["write_bytes"], "fetch %.0f + write %.0f B (copy-calibrated, %s)" % (
                 v["fetch_bytes"], v["write_bytes"], os.path.basename(path))
     return None, None
@@ -191,13 +192,15 @@ def bench_topk(args):
     ms = e0.elapsed_time(e1) / args.steps
     algo = T * N * 4 + T * k * 4
     achieved = algo / (ms * 1e-3) / 1e9
+    traffic, traffic_note = counted_traffic("topk_4096x65536", "smla_topk.hip", "smla_topk_kernel")
     res = {"metric": "sparse MLA indexer top-k: query rows/s", "value": round(T / (ms * 1e-3), 1),
            "unit": "query-rows/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "f32", "data": "synthetic (seeded device N(0,1))",
            "config": {"workload": "topk_4096x65536", "num_rows": T, "num_keys": N, "k": k},
            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                        "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                        "traffic": None if traffic is None else round(traffic), "traffic_note": traffic_note,
                         "kernel": "smla_topk_kernel", "kernel_us": round(ms * 1e3, 2),
                         "algorithmic_bytes": algo}}
     print(json.dumps(res), flush=True)
