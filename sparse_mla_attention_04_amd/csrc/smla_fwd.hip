@@ -21,7 +21,9 @@
 //   * online softmax in base 2 with wave-level reductions (max over the four
 //     lanes that share a head);
 //   * P.V: O^T += V^T . P^T on MFMA, V^T read straight from the same LDS
-//     tile with ds_read_b64_tr_b16 (the transposing LDS read of gfx950);
+//     tile with ds_read_b64_tr_b16 (the transposing LDS read of gfx950); the
+//     pipelined h = 64 kernels use v_mfma_f32_32x32x16_bf16 there (half the
+//     MFMA instructions of 16x16x32 for the same work);
 //   * waves that split the rows of one query are merged through LDS at the
 //     end; a split work-group writes its fp32 partial (normalised output
 //     and lse) to the caller's workspace instead, and a second kernel merges
@@ -52,6 +54,7 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 
@@ -118,6 +121,9 @@ struct Shape {
   // from LDS feeds two MFMAs; the two waves holding one head's row halves share
   // its exponent reference and add their row sums at the end.
   static constexpr bool RSPLIT = RSPLIT_;
+  // PV32 (pipelined, without RSPLIT): P.V on v_mfma_f32_32x32x16_bf16, each
+  // wave's 128 output dims x 64 heads as 4 x 2 accumulators of 32 x 32
+  static constexpr bool PV32 = PIPE_ && !RSPLIT_;
   static constexpr int NE = RSPLIT ? 2 : 1;            // 16-head groups in a wave's scores
   static constexpr int HEAD_GROUPS = PAIR ? 1 : HG;   // 16-head groups the shape covers
   // per-wave counts (NW x 8 words) at CNT_OFF.  The pipelined shapes keep the
@@ -528,9 +534,16 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
     for (int p = 0; p < 8; ++p) tr8ofs[p] = (uint32_t)(rr * 8 + (p ^ swr)) * 16u + (uint32_t)(n & 1) * 8u;
   }
 
-  f32x4 o[32];
+  f32x4 o[S::PV32 ? 1 : 32];
 #pragma unroll
-  for (int f = 0; f < 32; ++f) o[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int f = 0; f < (S::PV32 ? 1 : 32); ++f) o[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // PV32: accumulator (db, hb) = o16[2 * db + hb]: lane l holds head (or dense
+  // slot) 32 hb + (l & 31), dims 128 * hg + 32 db + 8 * (i >> 2) + 4 * (l >> 5) + (i & 3)
+  f32x16 o16[S::PV32 ? 8 : 1];
+#pragma unroll
+  for (int k = 0; k < (S::PV32 ? 8 : 1); ++k)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o16[k][i] = 0.f;
   // per 16-head group of the wave's scores (lane n: head n of the group)
   float m_run[S::NE], l_run[S::NE];       // exponent reference and row sum
   float m_seen[S::NE];                    // true running maximum
@@ -1230,6 +1243,22 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
             (LDS_AS bf16x4*)(tpd + vofs[1][f & 3] + (f >> 2) * S::RT * 128));
         return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
       };
+      // PV32: V^T operand k = 4 ks + db of tile itv: lane (b, n) = (lane >> 4,
+      // lane & 15) holds dim 32 db + 16 (b & 1) + n of the wave's 128 and the
+      // eight rows of P's writer lane group g = 2 ks + (b >> 1): 4g + j, 16 + 4g + j
+      auto read_vt32 = [&](int itv, int k) -> bf16x8 {
+        const int ks = k >> 2, db = k & 3;
+        const int b = lane >> 4, cq = n & 3;
+        const int g = 2 * ks + (b >> 1);
+        const int r0 = 4 * g + (n >> 2);
+        const int G = 2 * db + (b & 1);
+        const uint32_t col = (uint32_t)(G >> 2) * S::RT * 128u +
+                             (uint32_t)(((2 * (G & 3) + (cq >> 1)) ^ swz<S::FP8>(r0)) * 16 + (cq & 1) * 8);
+        const LDS_AS uint8_t* tpd = tptr(itv) + hg * 2 * S::RT * 128 + col;
+        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(tpd + r0 * 128));
+        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(tpd + (r0 + 16) * 128));
+        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
 
       if (nit > 0) {
         // (the row-half split variant issues a full ring even past the list:
@@ -1267,7 +1296,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         publish(softmax(0, sc, true), 0);   // P of tile 0
         bf16x8 vpre[8];
 #pragma unroll
-        for (int f = 0; f < 8; ++f) vpre[f] = read_vt(0, f);
+        for (int f = 0; f < 8; ++f) vpre[f] = S::PV32 ? read_vt32(0, f) : read_vt(0, f);
         // step it; REFILL: the gathers of tile it + NST (all but the last NST
         // steps), so those steps keep a full ring and wait on a constant count
         auto step = [&](int it, auto refill_tag) {
@@ -1292,7 +1321,16 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
           // reads took slots of the K operand ring's first group of reads
           bf16x8 pall[4];
 #pragma unroll
-          for (int hf = 0; hf < 4; ++hf) pall[hf] = pex[(it & 1) * 256 + hf * 64 + lane];
+          for (int hf = 0; hf < 4; ++hf) {
+            if constexpr (S::PV32) {
+              // B operand (hb, ks) = pall[2 * hb + ks]: head 32 hb + (lane & 31),
+              // the rows of writer lane group 2 ks + (lane >> 5)
+              const int hb = hf >> 1, ks = hf & 1;
+              pall[hf] = pex[(it & 1) * 256 + (2 * hb + ((lane & 31) >> 4)) * 64 + (2 * ks + (lane >> 5)) * 16 + (lane & 15)];
+            } else {
+              pall[hf] = pex[(it & 1) * 256 + hf * 64 + lane];
+            }
+          }
           // P.V of tile it over this wave's 8 output fragments x 4 head groups;
           // each fragment's V^T registers are refilled from tile it+1 once used;
           // the gathers of tile it + NST (into tile it's slot, free since the
@@ -1305,10 +1343,18 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
           sm_init(st);
 #pragma unroll
           for (int f = 0; f < 8; ++f) {
+            if constexpr (S::PV32) {
+              const int ks = f >> 2, db = f & 3;
 #pragma unroll
-            for (int hf = 0; hf < 4; ++hf)
-              o[4 * f + hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vpre[f], pall[hf], o[4 * f + hf], 0, 0, 0);
-            vpre[f] = read_vt(it + 1, f);
+              for (int hb = 0; hb < 2; ++hb)
+                o16[2 * db + hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vpre[f], pall[2 * hb + ks], o16[2 * db + hb], 0, 0, 0);
+              vpre[f] = read_vt32(it + 1, f);
+            } else {
+#pragma unroll
+              for (int hf = 0; hf < 4; ++hf)
+                o[4 * f + hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vpre[f], pall[hf], o[4 * f + hf], 0, 0, 0);
+              vpre[f] = read_vt(it + 1, f);
+            }
             // tiles before the last NST are whole (only the last listed tile
             // can be partial): no masking in the refill steps
             using MT = std::integral_constant<bool, !REFILL || S::RSPLIT || S::DENSE>;
@@ -1404,7 +1450,11 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
   for (int e = 0; e < S::NE; ++e) l_run[e] = 0.f;
   overflow = false;
 #pragma unroll
-  for (int f = 0; f < 32; ++f) o[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int f = 0; f < (S::PV32 ? 1 : 32); ++f) o[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < (S::PV32 ? 8 : 1); ++k)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o16[k][i] = 0.f;
   }
 
   // ---- epilogue: merge the row groups of each head group, normalise, write
@@ -1430,6 +1480,51 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
     // dims 128 * wave + 16f + 4 * g4 .. +3 of head (or dense slot) 16hf + n.
     __syncthreads();   // the statistics are visible
     const bool split = a.write_partials != 0;
+    if constexpr (S::PV32) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const int m = 32 * hb + (lane & 31);
+        const int sa = m >> 4, nn = m & 15;
+        const float M = stat[(sa * 16 + nn) * 2];
+        const float L = (M != NEG_INF) ? stat[(sa * 16 + nn) * 2 + 1] : 0.f;
+        const bool empty = !(L > 0.f);
+        const float inv = empty ? 0.f : 1.f / L;
+        const float lse_v = empty ? NEG_INF : (M + __log2f(L)) * LN2;
+        int orow = t, ohead = m;
+        bool ok = m < a.h;
+        if constexpr (S::DENSE) {
+          const int r = m / a.h;
+          ok = r < d_nr;
+          orow = d_r0 + r;
+          ohead = m - r * a.h;
+        }
+        if (!ok) continue;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int d0 = 128 * hg + 32 * db + 8 * q + 4 * (lane >> 5);
+            const f32x16 v = o16[2 * db + hb];
+            if (!split) {
+              u32x2 pk;
+              pk[0] = (uint32_t)f32_to_bf16_bits(v[4 * q] * inv) | ((uint32_t)f32_to_bf16_bits(v[4 * q + 1] * inv) << 16);
+              pk[1] = (uint32_t)f32_to_bf16_bits(v[4 * q + 2] * inv) | ((uint32_t)f32_to_bf16_bits(v[4 * q + 3] * inv) << 16);
+              *reinterpret_cast<u32x2*>(a.out + (int64_t)orow * a.out_st + (int64_t)ohead * a.out_sh + d0) = pk;
+            } else {
+              f32x4 w;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) w[j] = v[4 * q + j] * inv;
+              *reinterpret_cast<f32x4*>(a.ws_out + (unit * a.h + ohead) * D_V + d0) = w;
+            }
+          }
+        }
+        if (hg == 0 && lane < 32) {
+          if (!split) a.lse[(int64_t)orow * a.lse_st + ohead] = lse_v;
+          else a.ws_lse[unit * a.h + ohead] = lse_v;
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int hf = 0; hf < 4; ++hf) {
       const int sa = S::RSPLIT ? 2 * hf : hf;   // statistics slot(s) of head group hf
