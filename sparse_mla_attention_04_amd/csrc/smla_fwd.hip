@@ -538,7 +538,8 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
 #pragma unroll
   for (int f = 0; f < (S::PV32 ? 1 : 32); ++f) o[f] = f32x4{0.f, 0.f, 0.f, 0.f};
   // PV32: accumulator (db, hb) = o16[2 * db + hb]: lane l holds head (or dense
-  // slot) 32 hb + (l & 31), dims 128 * hg + 32 db + 8 * (i >> 2) + 4 * (l >> 5) + (i & 3)
+  // slot) 32 hb + (l & 31) and, for i = 4q + j, dim 128 hg + 64 (db >> 1) +
+  // 16 ((db & 1) + 2 (q >> 1)) + 8 (q & 1) + 4 (l >> 5) + j
   f32x16 o16[S::PV32 ? 8 : 1];
 #pragma unroll
   for (int k = 0; k < (S::PV32 ? 8 : 1); ++k)
@@ -1244,16 +1245,20 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
       };
       // PV32: V^T operand k = 4 ks + db of tile itv: lane (b, n) = (lane >> 4,
-      // lane & 15) holds dim 32 db + 16 (b & 1) + n of the wave's 128 and the
-      // eight rows of P's writer lane group g = 2 ks + (b >> 1): 4g + j, 16 + 4g + j
+      // lane & 15) holds dim 64 (db >> 1) + 16 ((db & 1) + 2 (b & 1)) + n of the
+      // wave's 128 and the eight rows of P's writer lane group g = 2 ks + (b >> 1):
+      // 4g + j, 16 + 4g + j
       auto read_vt32 = [&](int itv, int k) -> bf16x8 {
         const int ks = k >> 2, db = k & 3;
         const int b = lane >> 4, cq = n & 3;
         const int g = 2 * ks + (b >> 1);
         const int r0 = 4 * g + (n >> 2);
-        const int G = 2 * db + (b & 1);
-        const uint32_t col = (uint32_t)(G >> 2) * S::RT * 128u +
-                             (uint32_t)(((2 * (G & 3) + (cq >> 1)) ^ swz<S::FP8>(r0)) * 16 + (cq & 1) * 8);
+        // 16-dim group p of line db >> 1: the block's two halves sit in the
+        // line's chunks 0..3 and 4..7, so that lanes 0..31 (four rows, both
+        // halves) hit sixteen distinct bank groups under the r & 7 swizzle
+        const int p = (db & 1) + 2 * (b & 1);
+        const uint32_t col = (uint32_t)(db >> 1) * S::RT * 128u +
+                             (uint32_t)(((2 * p + (cq >> 1)) ^ swz<S::FP8>(r0)) * 16 + (cq & 1) * 8);
         const LDS_AS uint8_t* tpd = tptr(itv) + hg * 2 * S::RT * 128 + col;
         const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(tpd + r0 * 128));
         const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(tpd + (r0 + 16) * 128));
@@ -1503,7 +1508,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         for (int db = 0; db < 4; ++db) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int d0 = 128 * hg + 32 * db + 8 * q + 4 * (lane >> 5);
+            const int d0 = 128 * hg + 64 * (db >> 1) + 16 * ((db & 1) + 2 * (q >> 1)) + 8 * (q & 1) + 4 * (lane >> 5);
             const f32x16 v = o16[2 * db + hb];
             if (!split) {
               u32x2 pk;
