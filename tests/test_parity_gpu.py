@@ -142,7 +142,7 @@ def test_repeated_index_returns_the_row(k, splits):
     check(out, lse, ro, rl, "repeated index")
 
 
-@pytest.mark.parametrize("splits,h,variant", [(1, 16, 0), (3, 16, 0), (1, 64, 2), (3, 64, 2),
+@pytest.mark.parametrize("splits,h,variant", [(1, 16, 0), (3, 16, 0), (1, 64, 2), (3, 64, 2), (1, 64, 0), (3, 64, 0),
                                              (1, 8, 2), (3, 8, 2), (1, 32, 2), (3, 32, 2)])
 def test_large_score_spread_recomputes_exactly(splits, h, variant):
     """A row whose later entries score far above its first tile (beyond the
@@ -929,6 +929,47 @@ def test_dense_matches_oracle(h, rope):
     ro, rl = O.sparse_mla_forward(c.q, c.kv, idx, topk=idx.shape[1], scale=c.scale, index_mode="logical",
                                   block_table=c.block_table, token_seq=c.token_seq)
     check(out, lse, ro, rl, "dense h=%d rope=%d" % (h, rope))
+
+
+@pytest.mark.parametrize("rope", [64, 0])
+def test_dense_large_score_spread_recomputes(rope):
+    """Dense causal mode with a cache row far above the others at a late
+    position: rows whose prefix reaches it see it only in a later tile, past
+    the first tile's exponent headroom (the recomputation pass, per block)."""
+    say("dense score spread", rope)
+    c = G.build_case("dense_spread", seed=85, hist=[0, 0], new=[700, 300], num_heads=8, topk=8, rope_dims=rope)
+    d = 576 if rope else 512
+    kv = c.kv.copy()
+    flat = kv.reshape(-1, d)
+    qsign = np.sign((c.q[0, 0].astype(np.uint32) << 16).view(np.float32))
+    hot = int(c.block_table[0, 500 // c.page_size]) * c.page_size + 500 % c.page_size   # position 500 of sequence 0
+    flat[hot] = G.to_bf16_bits((16.0 * qsign).astype(np.float32))
+    c2 = G.Case(**{**c.__dict__, "kv": kv})
+    qs, pos, idx = _dense_inputs(c2)
+    out, lse = _run_dense(c2, qs, pos)
+    from oracle import sparse_mla_oracle as O
+    ro, rl = O.sparse_mla_forward(c2.q, c2.kv, idx, topk=idx.shape[1], scale=c2.scale, index_mode="logical",
+                                  block_table=c2.block_table, token_seq=c2.token_seq)
+    check(out, lse, ro, rl, "dense spread rope=%d" % rope)
+
+
+@pytest.mark.parametrize("splits", [1, 2])
+def test_nope_h64_large_score_spread_recomputes(splits):
+    """NoPE rows at h = 64 (the pipelined kernel) with the recomputation pass."""
+    say("nope h64 spread", splits)
+    c = G.make_mini(seed=77, num_heads=64, topk=300, drop_frac=0.0, rope_dims=0)
+    kv = c.kv.copy()
+    flat = kv.reshape(-1, 512)
+    hot = 9
+    qsign = np.sign((c.q[0, 0].astype(np.uint32) << 16).view(np.float32))
+    flat[hot] = G.to_bf16_bits((16.0 * qsign).astype(np.float32))
+    c2 = G.Case(**{**c.__dict__, "kv": kv})
+    sidx = slot_indices(c2)
+    sidx[:, -1] = hot
+    from oracle import sparse_mla_oracle as O
+    ro, rl = O.sparse_mla_forward(c2.q, c2.kv, sidx, topk=c2.topk, scale=c2.scale, index_mode="slot")
+    out, lse = to_np(*run_gpu(Dev(c2, idx=sidx), logical=False, num_splits=splits))
+    check(out, lse, ro, rl, "nope h64 spread s%d" % splits)
 
 
 def test_dense_unsorted_positions_empty_sequence_and_bad_page():
