@@ -256,16 +256,27 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
   return bf16x8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
 }
 
-// XOR swizzle of the 16-byte chunks of tile row r (3 bits), chosen per cache
-// format from LDS bank-conflict counts measured on gfx950 for each access
-// pattern of the kernels:
-//   bf16 tiles (16-row K operand reads of one chunk; 4-row x 2-chunk
-//     transposing V reads): r & 7 leaves both conflict-free;
-//   fp8 tiles (transposing reads of rows 4g + j and 16 + 4g + j): rows r and
-//     r + 16 must differ, which r & 7 does not give.
+// XOR swizzle of the 16-byte chunks of tile row r (3 bits).  gfx950's LDS
+// has 64 banks (256 B); measured with single-pattern probes, an 8-byte read
+// (plain or transposing) serves lanes 0-31 and then 32-63, and a 16-byte read
+// serves the lane sets {0-7, 24-31}, {8-23}, {32-39, 56-63}, {40-55} one per
+// cycle.  A tile row is 128 B, so the bank group of chunk c of row r is
+// 8 (r & 1) + (c ^ swz(r)), and each cycle's lanes need distinct groups:
+//   bf16 tiles (16-row K operand reads of one chunk per lane group; 4-row x
+//     2-chunk transposing V reads; the 32x32 P.V reads, which take rows r0
+//     and r0 + 16 with the swizzle of r0): r & 7 is conflict-free for all;
+//   fp8 tiles (the same K reads; transposing reads of rows 4g + j and
+//     16 + 4g + j): the K reads put rows r and r + 8 in one cycle with chunks
+//     c and c ^ 1, the transposing reads rows r and r + 16 with one chunk.
+// Bit 2 of the swizzle also decides, for each row of a gather instruction,
+// which 64-byte half of the row's line its first four lanes fetch.  On the
+// 640-byte fp8 rows, gathers ran 4% faster when that bit follows row bit 1
+// (or 0) than when it follows row bit 2 or is constant; bf16 and the 512-byte
+// NoPE rows showed no difference.  Among the conflict-free fp8 swizzles this
+// one takes bit 2 from row bit 1.
 template <bool FP8>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (FP8) return (((r >> 1) & 1) << 1) | (((r >> 2) & 1) << 2) | (((r >> 3) ^ (r >> 4)) & 1);
+  if constexpr (FP8) return ((r & 2) << 1) | ((r & 4) >> 1) | ((r >> 4) & 1);
   else return r & 7;
 }
 
