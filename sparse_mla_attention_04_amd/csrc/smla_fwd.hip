@@ -227,6 +227,13 @@ __device__ __forceinline__ float max_xor16_32(float v) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// two floats to a packed bf16 pair (round to nearest even), one instruction
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{lo, hi}, bf16x2v));
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   __bf16 b = (__bf16)x;
   return __builtin_bit_cast(uint16_t, b);
@@ -1497,6 +1504,12 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
     __syncthreads();   // the statistics are visible
     const bool split = a.write_partials != 0;
     if constexpr (S::PV32) {
+      // lane l holds slot (head, or dense slot) m = 32 hb + (l & 31) and, in
+      // accumulator (db, hb) at i = 4q + j, dim dl + j of the wave's 128 with
+      // dl = 64 (db >> 1) + 16 ((db & 1) + 2 (q >> 1)) + 8 (q & 1) + 4 (l >> 5)
+      float inv[2];
+      int64_t obase[2];
+      bool okv[2];
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
         const int m = 32 * hb + (lane & 31);
@@ -1504,7 +1517,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         const float M = stat[(sa * 16 + nn) * 2];
         const float L = (M != NEG_INF) ? stat[(sa * 16 + nn) * 2 + 1] : 0.f;
         const bool empty = !(L > 0.f);
-        const float inv = empty ? 0.f : 1.f / L;
+        inv[hb] = empty ? 0.f : 1.f / L;
         const float lse_v = empty ? NEG_INF : (M + __log2f(L)) * LN2;
         int orow = t, ohead = m;
         bool ok = m < a.h;
@@ -1514,29 +1527,58 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
           orow = d_r0 + r;
           ohead = m - r * a.h;
         }
-        if (!ok) continue;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int d0 = 128 * hg + 64 * (db >> 1) + 16 * ((db & 1) + 2 * (q >> 1)) + 8 * (q & 1) + 4 * (lane >> 5);
-            const f32x16 v = o16[2 * db + hb];
-            if (!split) {
-              u32x2 pk;
-              pk[0] = (uint32_t)f32_to_bf16_bits(v[4 * q] * inv) | ((uint32_t)f32_to_bf16_bits(v[4 * q + 1] * inv) << 16);
-              pk[1] = (uint32_t)f32_to_bf16_bits(v[4 * q + 2] * inv) | ((uint32_t)f32_to_bf16_bits(v[4 * q + 3] * inv) << 16);
-              *reinterpret_cast<u32x2*>(a.out + (int64_t)orow * a.out_st + (int64_t)ohead * a.out_sh + d0) = pk;
-            } else {
-              f32x4 w;
-#pragma unroll
-              for (int j = 0; j < 4; ++j) w[j] = v[4 * q + j] * inv;
-              *reinterpret_cast<f32x4*>(a.ws_out + (unit * a.h + ohead) * D_V + d0) = w;
-            }
-          }
-        }
-        if (hg == 0 && lane < 32) {
+        okv[hb] = ok;
+        obase[hb] = split ? (unit * a.h + ohead) * D_V : (int64_t)orow * a.out_st + (int64_t)ohead * a.out_sh;
+        if (ok && hg == 0 && lane < 32) {
           if (!split) a.lse[(int64_t)orow * a.lse_st + ohead] = lse_v;
           else a.ws_lse[unit * a.h + ohead] = lse_v;
+        }
+      }
+      if (!split) {
+        // bf16 output in 16-byte pieces: for q = 2r, 2r + 1 a lane holds dims
+        // dl .. dl + 3 of both; one lane-half swap gives lane l < 32 the two
+        // pieces of q = 2r (dims dl .. dl + 7) and lane l + 32 those of q = 2r + 1,
+        // so each store instruction writes 32 contiguous bytes per slot.  With
+        // 8-byte stores straight from the accumulators the epilogue was 2%
+        // of c4's kernel time slower.
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          if (!okv[hb]) continue;
+          uint16_t* ob = a.out + obase[hb] + 128 * hg + 8 * (lane >> 5);
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int qp = 0; qp < 4; qp += 2) {
+              const f32x16& v = o16[2 * db + hb];
+              uint32_t r0[2], r1[2];
+              r0[0] = pack_bf16x2(v[4 * qp] * inv[hb], v[4 * qp + 1] * inv[hb]);
+              r0[1] = pack_bf16x2(v[4 * qp + 2] * inv[hb], v[4 * qp + 3] * inv[hb]);
+              r1[0] = pack_bf16x2(v[4 * qp + 4] * inv[hb], v[4 * qp + 5] * inv[hb]);
+              r1[1] = pack_bf16x2(v[4 * qp + 6] * inv[hb], v[4 * qp + 7] * inv[hb]);
+#pragma unroll
+              for (int w = 0; w < 2; ++w) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(r0[w], r1[w], false, false);
+                r0[w] = sw[0];
+                r1[w] = sw[1];
+              }
+              *reinterpret_cast<u32x4*>(ob + 64 * (db >> 1) + 16 * ((db & 1) + 2 * (qp >> 1))) = u32x4{r0[0], r0[1], r1[0], r1[1]};
+            }
+        }
+      } else {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          if (!okv[hb]) continue;
+          float* wb = a.ws_out + obase[hb] + 128 * hg + 4 * (lane >> 5);
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const f32x16& v = o16[2 * db + hb];
+              f32x4 w;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) w[j] = v[4 * q + j] * inv[hb];
+              *reinterpret_cast<f32x4*>(wb + 64 * (db >> 1) + 16 * ((db & 1) + 2 * (q >> 1)) + 8 * (q & 1)) = w;
+            }
         }
       }
       return;
