@@ -62,6 +62,20 @@ constexpr int MIN_RANK = 48;
 // [j * per, (j + 1) * per); suffix sums over the threads locate the owner of
 // the crossing bin, which writes ctl[0] = bin, ctl[1] = keys still to take
 // inside it, ctl[4] = the bin's count.  Ends with a barrier.
+// Inclusive prefix sum over a wave's 64 lanes without LDS: shifts by 1, 2,
+// 4 and 8 lanes inside each 16-lane row (lanes with no source add 0), then
+// row 0's total into row 1 and row 2's into row 3 (broadcast of lanes 15 and
+// 47), then the first two rows' total into rows 2 and 3 (lane 31).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return x;
+}
+
 __device__ __forceinline__ void find_bin(const uint32_t* hist, int nb, int kr, int* ctl, int* wsum, int tid,
                                          int lane, int wave) {
   const int per = nb / 256;
@@ -235,8 +249,11 @@ __global__ void __launch_bounds__(256) smla_topk_kernel(TopkArgs a) {
       kr = (int)rank;
       lds_select(ns, 0);
       const uint32_t tau = prefix;                    // the sample's rank-th largest key
-      // one pass: every key >= tau to LDS, one LDS atomic per wave and
-      // sixteen scores (wave-aggregated appends in index order within a lane)
+      // one pass: every key >= tau to LDS.  Per batch of 4U keys per lane, the
+      // lanes count their keys >= tau, a wave prefix sum gives each lane its
+      // place, and one LDS atomic per wave reserves the wave's range (about
+      // 5% of keys pass, so a per-key atomic ran in nearly every key slot of
+      // every wave, each waiting for its return)
       __syncthreads();
       if (tid == 0) ctl[3] = 0;
       __syncthreads();
@@ -266,12 +283,39 @@ __global__ void __launch_bounds__(256) smla_topk_kernel(TopkArgs a) {
       if (n4 > 0) load_batch(0, cur);
       for (int j0 = 0; j0 < n4; j0 += 256 * U) {
         if (j0 + 256 * U < n4) load_batch(j0 + 256 * U, nxt);
+        uint32_t key[U][4];
+        int cnt = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const bool ok = j0 + u * 256 + tid < n4;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            key[u][q] = order_key(cur[u][q]);
+            cnt += (ok && key[u][q] >= tau) ? 1 : 0;
+          }
+        }
+        const int incl = wave_incl_scan(cnt);
+        const int total = __builtin_amdgcn_readlane(incl, 63);
+        int base = 0;
+        if (total > 0) {
+          if (lane == 0) base = atomicAdd(&ctl[3], total);
+          base = __builtin_amdgcn_readfirstlane(base);
+        }
+        int pos = base + incl - cnt;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int j = j0 + u * 256 + tid;
           const bool ok = j < n4;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) append(order_key(cur[u][q]), 4 * j + q, ok);
+          for (int q = 0; q < 4; ++q) {
+            if (ok && key[u][q] >= tau) {
+              if (pos < CAP) {
+                cand_key[pos] = key[u][q];
+                cand_idx[pos] = 4 * j + q;
+              }
+              ++pos;
+            }
+          }
         }
         if (j0 + 256 * U < n4) {
 #pragma unroll
