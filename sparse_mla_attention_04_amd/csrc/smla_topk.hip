@@ -7,15 +7,17 @@
 // One work-group (four waves) per query row.  The k-th largest score is found
 // by a radix select over an order-preserving 32-bit key.
 //   One read (long rows): every 32nd 128-byte line of the row is read as a
-//   sample, and the sample's r-th largest key tau is found in LDS, r chosen
-//   so that about (k + CAP) / 2 keys of the row are expected at or above it.
+//   sample, and a threshold tau is found in LDS: the lowest key of the 22-bit
+//   bucket holding the sample's r-th largest key, r chosen so that about
+//   (k + CAP) / 2 keys of the row are expected at or above it.
 //   One pass over the row then copies every key >= tau (and its index) to
 //   LDS.  When k <= that count <= CAP, the candidates hold the whole top-k and
 //   every key equal to the k-th, and the selection finishes in LDS.  Any
 //   other count (an unrepresentative sample) takes the two-read route below.
 //   Measured on MI355X (4096 rows x 65536 N(0,1) scores, k = 2048): 0.476 ms
 //   with two reads, 0.474 ms with one read while each wave kept one load in
-//   flight, 0.339 ms with one read in batches of eight loads per thread.
+//   flight, 0.339 ms with one read in batches of eight loads per thread,
+//   0.296 ms with the candidates appended one LDS atomic per wave and batch.
 //   Two reads: an LDS histogram of the key's top 11 bits over the whole row
 //   names the bucket holding the k-th key.  When that bucket fits in LDS, a
 //   second read of the row writes every key above the bucket and copies the
@@ -163,8 +165,8 @@ __global__ void __launch_bounds__(256) smla_topk_kernel(TopkArgs a) {
   // radix select over the nc LDS candidates: with (prefix, mask, kr) on entry
   // describing the keys still open, leaves prefix = the kr-th largest key,
   // kr = how many keys equal to it are taken, ctl[4] = how many there are
-  auto lds_select = [&](int nc, int first_pass) {
-    for (int pass = first_pass; pass < 3; ++pass) {
+  auto lds_select = [&](int nc, int first_pass, int end_pass = 3) {
+    for (int pass = first_pass; pass < end_pass; ++pass) {
       const int shift = SHIFTS[pass];
       const int nb = 1 << WIDTHS[pass];
       for (int i = tid; i < nb; i += 256) hist[i] = 0u;
@@ -217,13 +219,28 @@ __global__ void __launch_bounds__(256) smla_topk_kernel(TopkArgs a) {
       ctl[3] = 0;
     }
     __syncthreads();
-    for (int c = tid; c < nc; c += 256) {
-      const uint32_t u = cand_key[c];
-      if (u > prefix) {
-        out[atomicAdd(&ctl[2], 1)] = cand_idx[c];
-      } else if (u == prefix && ~(uint32_t)cand_idx[c] >= vsel) {
-        out[(k - kr) + atomicAdd(&ctl[3], 1)] = cand_idx[c];
+    // wave-aggregated output slots: one atomic per wave and kind of key
+    for (int c0 = 0; c0 < nc; c0 += 256) {
+      const int c = c0 + tid;
+      uint32_t u = 0u;
+      int ix = 0;
+      if (c < nc) {
+        u = cand_key[c];
+        ix = cand_idx[c];
       }
+      const int above = (c < nc && u > prefix) ? 1 : 0;
+      const int tie = (c < nc && u == prefix && ~(uint32_t)ix >= vsel) ? 1 : 0;
+      const int ia = wave_incl_scan(above), it = wave_incl_scan(tie);
+      const int ta = __builtin_amdgcn_readlane(ia, 63), tt = __builtin_amdgcn_readlane(it, 63);
+      int ba = 0, bt = 0;
+      if (lane == 0) {
+        if (ta > 0) ba = atomicAdd(&ctl[2], ta);
+        if (tt > 0) bt = atomicAdd(&ctl[3], tt);
+      }
+      ba = __builtin_amdgcn_readfirstlane(ba);
+      bt = __builtin_amdgcn_readfirstlane(bt);
+      if (above) out[ba + ia - 1] = ix;
+      else if (tie) out[(k - kr) + bt + it - 1] = ix;
     }
   };
 
@@ -247,8 +264,11 @@ __global__ void __launch_bounds__(256) smla_topk_kernel(TopkArgs a) {
       }
       __syncthreads();
       kr = (int)rank;
-      lds_select(ns, 0);
-      const uint32_t tau = prefix;                    // the sample's rank-th largest key
+      // two of the three digits: tau is the lowest key of the 22-bit bucket
+      // holding the sample's rank-th largest key (a threshold only needs to
+      // be about right; the bucket spans 2^-13 of a score's magnitude)
+      lds_select(ns, 0, 2);
+      const uint32_t tau = prefix;
       // one pass: every key >= tau to LDS.  Per batch of 4U keys per lane, the
       // lanes count their keys >= tau, a wave prefix sum gives each lane its
       // place, and one LDS atomic per wave reserves the wave's range (about
