@@ -83,13 +83,11 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, int nb, int kr, i
   const int per = nb / 256;
   int own = 0;
   for (int q = 0; q < per; ++q) own += (int)hist[tid * per + q];
-  // inclusive suffix sum over thread index, high to low
-  int incl = own;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int v = __shfl_down(incl, d, 64);
-    if (lane + d < 64) incl += v;
-  }
+  // inclusive suffix sum over thread index, high to low: the wave's total
+  // minus the inclusive prefix sum, plus the lane's own count
+  const int pre = wave_incl_scan(own);
+  const int wtot = __builtin_amdgcn_readlane(pre, 63);
+  const int incl = wtot - pre + own;
   if (lane == 0) wsum[wave] = incl;   // the wave's total
   __syncthreads();
   int above_waves = 0;
