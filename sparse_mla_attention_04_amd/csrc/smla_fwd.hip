@@ -349,11 +349,14 @@ __device__ __forceinline__ uint32_t field16(const uint32_t (&w)[8], int g) {
 //     physical row (slot >> bucket_shift), list order inside a group, so the
 //     rows that run together on one XCD read nearby cache rows.  Counts are
 //     packed two groups per 32-bit word (each at most 2048 per pass).
-template <int NW, int EPT>
+//   after_lookups() runs once every entry's lookup has landed and before the
+//   first barrier: loads issued there are not waited for by the compaction.
+template <int NW, int EPT, class AfterLookups>
 __device__ __forceinline__ int compact_chunk(const FwdArgs& a, const int (&raw)[EPT], int seq_ok, int64_t bt_row,
-                                             int* list, int* wcnt, int wave, int lane) {
+                                             int* list, int* wcnt, int wave, int lane, AfterLookups&& after_lookups) {
   int sl[EPT];
   translate_all<EPT>(a, raw, seq_ok, bt_row, sl);
+  after_lookups();
   int cnt = 0;
 #pragma unroll
   for (int i = 0; i < EPT; ++i) cnt += (sl[i] >= 0);
@@ -594,8 +597,20 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
   // ---- queries of this wave's 16 heads, in the MFMA B-operand layout:
   //      lane (g4, n) holds head hg*16+n, dims 32*kk + 8*g4 .. +7
   bf16x8 qb[18 * S::NE];   // RSPLIT: group e's k-step kk at qb[18e + kk]
+  // QDMA (pipelined h = 64 shapes, not dense): the queries (64 heads x 576
+  // dims = two tiles' bytes) are not loaded here.  Loads retire in issue order
+  // on one counter, so the compaction's wait for its block-table words would
+  // also wait for 73.7 KB of queries requested before them.  They are instead
+  // requested once those words have landed, straight into ring slots 2..3
+  // (idle until the first tiles are gathered), and read into registers after
+  // tiles 0..1 are issued and before slots 2..3 are.
+  constexpr bool QDMA = S::PV32 && !S::DENSE;
+  if constexpr (QDMA) {
 #pragma unroll
-  for (int e = 0; e < S::NE; ++e) {
+    for (int kk = 0; kk < 18; ++kk) qb[kk] = bf16x8{};
+  }
+#pragma unroll
+  for (int e = 0; e < (QDMA ? 0 : S::NE); ++e) {
     const int head = (S::RSPLIT ? 32 * (wave >> 1) + 16 * e : (S::PAIR ? 0 : hg) * 16) + n;
     if (S::DENSE || head < a.h) {
       const uint16_t* qp = S::DENSE ? a.q + (int64_t)(d_r0 + d_row) * a.q_st + (int64_t)d_head * a.q_sh + 8 * g4
@@ -674,7 +689,41 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
       n_valid = pmax + 1;
     } else {
       if (cs != c0 || pass != 0) load_raw(cs, ce);
-      n_valid = compact_chunk<S::NW, S::EPT>(a, raw, seq_ok, bt_row, list, wcnt, wave, lane);
+      n_valid = compact_chunk<S::NW, S::EPT>(a, raw, seq_ok, bt_row, list, wcnt, wave, lane, [&]() {
+        if constexpr (QDMA) {
+          if (cs == c0 && pass == 0) {
+            // lane (g4, n): head 16 hg + n, dims 32 kk + 8 g4 .. +7 -> slot
+            // bytes 2 TILE_BYTES + 1024 (KS hg + kk) + 16 lane (heads past h
+            // read head 0 and are zeroed when read out)
+            const int head = hg * 16 + n;
+            const uint16_t* qp = a.q + (int64_t)t * a.q_st + (int64_t)(head < a.h ? head : 0) * a.q_sh + 8 * g4;
+            const uint32_t qd = ring0 + 2u * S::TILE_BYTES + (uint32_t)(hg * S::KS) * 1024u;
+#pragma unroll
+            for (int kk = 0; kk < S::KS; ++kk) {
+              switch (kk) {   // dma16 writes LDS at m0 + offset + 16 lane
+                case 0: dma16<0>(qp, qd); break;
+                case 1: dma16<64>(qp, qd + 1 * 960); break;
+                case 2: dma16<128>(qp, qd + 2 * 960); break;
+                case 3: dma16<192>(qp, qd + 3 * 960); break;
+                case 4: dma16<256>(qp, qd + 4 * 960); break;
+                case 5: dma16<320>(qp, qd + 5 * 960); break;
+                case 6: dma16<384>(qp, qd + 6 * 960); break;
+                case 7: dma16<448>(qp, qd + 7 * 960); break;
+                case 8: dma16<512>(qp, qd + 8 * 960); break;
+                case 9: dma16<576>(qp, qd + 9 * 960); break;
+                case 10: dma16<640>(qp, qd + 10 * 960); break;
+                case 11: dma16<704>(qp, qd + 11 * 960); break;
+                case 12: dma16<768>(qp, qd + 12 * 960); break;
+                case 13: dma16<832>(qp, qd + 13 * 960); break;
+                case 14: dma16<896>(qp, qd + 14 * 960); break;
+                case 15: dma16<960>(qp, qd + 15 * 960); break;
+                case 16: dma16<1024>(qp, qd + 16 * 960); break;
+                default: dma16<1088>(qp, qd + 17 * 960); break;
+              }
+            }
+          }
+        }
+      });
     }
 
     // ---- tiles: tile i belongs to row group i % NRG
@@ -1283,11 +1332,48 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
         return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
       };
 
+      // QDMA: the queries out of slots 2..3 into registers (this wave's own
+      // loads have landed), then a barrier before any wave gathers into them
+      const bool qread = QDMA && cs == c0 && pass == 0;
+      auto read_q = [&]() {
+        if constexpr (QDMA) {
+          const LDS_AS uint8_t* qs = lds + 2 * S::TILE_BYTES + hg * S::KS * 1024 + 16 * lane;
+#pragma unroll
+          for (int kk = 0; kk < S::KS; ++kk) qb[kk] = *reinterpret_cast<const LDS_AS bf16x8*>(qs + 1024 * kk);
+          if (hg * 16 + n >= a.h) {
+#pragma unroll
+            for (int kk = 0; kk < S::KS; ++kk) qb[kk] = bf16x8{};
+          }
+          if (a.q_neg) {
+#pragma unroll
+            for (int kk = 0; kk < S::KS; ++kk)
+              qb[kk] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, qb[kk]) ^ 0x80008000u);
+          }
+          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        }
+      };
+      if (qread && nit == 0) {
+        wait_vm<0>();
+        read_q();
+      }
       if (nit > 0) {
         // (the row-half split variant issues a full ring even past the list:
         // its steps wait on a constant count)
+        constexpr int NPRE = QDMA ? 2 : S::NST;   // tiles gathered before the queries are read out
 #pragma unroll
-        for (int st = 0; st < S::NST; ++st) {
+        for (int st = 0; st < NPRE; ++st) {
+          if (S::RSPLIT || st < nit) {
+            dma_prep(st);
+#pragma unroll
+            for (int L = 0; L < S::NLINES; ++L) dma_line(L);
+          }
+        }
+        if (qread) {
+          wait_tiles<S::PER, S::NST>(nit < 2 ? nit : 2);
+          read_q();
+        }
+#pragma unroll
+        for (int st = NPRE; st < S::NST; ++st) {
           if (S::RSPLIT || st < nit) {
             dma_prep(st);
 #pragma unroll
