@@ -165,6 +165,7 @@ def cpu_baseline(case, seconds):
     el = time.perf_counter() - t0
     return {"value": round(done / el, 2), "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
             "cpu_model": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "extrapolated_full_config_s": float("%.3g" % (T * el / done)),
             "sample": "%d query rows of %s (random order over all %d rows) in %.1f s; numpy oracle in fp32 "
                       "(per-row Python gather, BLAS with %d threads)" % (done, case.name, T, el, threads)}
 
