@@ -234,6 +234,27 @@ def test_topk_above_one_compaction_pass():
     check(o2, l2, *oracle(c), what="topk 5000 split")
 
 
+@pytest.mark.parametrize("rope_dims,h", [(64, 64), (0, 64), (64, 48)])
+def test_h64_later_pass_after_empty_first_pass(rope_dims, h):
+    """33..64 heads (queries staged through LDS before the first tiles) with
+    top-k above one compaction pass: rows whose first 2048 entries are all -1
+    gather no tile in that pass and must still attend with their queries in
+    the next; other rows have an empty second pass, or no entry at all."""
+    say("h>32 empty first pass", rope_dims, h)
+    c = G.build_case("two_pass", seed=34, hist=[9000], new=[6], num_heads=h, topk=5000, drop_frac=0.05,
+                     rope_dims=rope_dims)
+    idx = c.topk_idx.copy()
+    idx[0::3, :2048] = -1
+    idx[1::3, 2048:] = -1
+    idx[5, :] = -1
+    c2 = G.Case(**{**c.__dict__, "topk_idx": idx})
+    ref = oracle(c2)
+    assert np.isneginf(ref[1][5]).all() and np.isfinite(ref[1][:5]).all()
+    for splits in (1, 2):
+        out, lse = to_np(*run_gpu(Dev(c2), num_splits=splits))
+        check(out, lse, *ref, what="h=%d rope=%d splits=%d" % (h, rope_dims, splits))
+
+
 def test_page_size_16():
     say("page size 16")
     c = G.make_mini(seed=31, num_heads=8, topk=300, page_size=16)
