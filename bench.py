@@ -17,7 +17,10 @@ caches, and the CPU oracle (fp32) timed on a bounded sample of the same
 workload on this host.  The same line carries two more measured workloads
 under their own keys, each with its own roofline: "c4_long_prefill"
 (16384 rows, h=64, bf16: the MFMA-bound target) and "c2_decode" (32 rows,
-h=8, split-KV + merge, also replayed from a HIP graph).
+h=8, split-KV + merge, also replayed from a HIP graph).  For context it also
+reports the rates plain torch copy and read kernels reach on this GPU
+("measured_bandwidth"); every roofline fraction stays against the published
+peak.
 
 Workloads (synthetic, seeded; `--workload` runs one of them alone):
   c5_fp8               32768 rows over 16 sequences (histories 8192..131072), h=8, fp8 cache
@@ -168,6 +171,36 @@ def cpu_baseline(case, seconds):
             "extrapolated_full_config_s": float("%.3g" % (T * el / done)),
             "sample": "%d query rows of %s (random order over all %d rows) in %.1f s; numpy oracle in fp32 "
                       "(per-row Python gather, BLAS with %d threads)" % (done, case.name, T, el, threads)}
+
+
+def measured_bandwidth(nbytes=1 << 31, reps=10):
+    """Rates of plain torch kernels on this GPU over 2 GiB (more than the L2s
+    and the MALL hold): a device copy (bytes read plus bytes written per
+    second) and a read-only reduction.  Context beside the published 8 TB/s
+    that roofline.frac is taken against; not used in any fraction."""
+    import torch
+    a = torch.zeros(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+
+    def rate(fn, moved):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return moved / (float(np.median(ts)) * 1e-3) / 1e9
+
+    copy = rate(lambda: b.copy_(a), 2 * nbytes)
+    read = rate(lambda: a.sum(), nbytes)
+    del a, b
+    torch.cuda.empty_cache()
+    return {"copy_GBps": round(copy, 1), "read_GBps": round(read, 1), "bytes": nbytes,
+            "kernels": "torch copy_ (read + write counted) and sum (read) over 2 GiB fp32, median of %d" % reps}
 
 
 def bench_topk(args):
@@ -582,6 +615,8 @@ def main():
         if k in res_main:
             res[k] = res_main[k]
     res.update(extras)
+    print("bench: measured bandwidth", file=sys.stderr, flush=True)
+    res["measured_bandwidth"] = measured_bandwidth()
     if not args.no_cpu_baseline:
         print("bench: cpu baseline", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(case_main, args.cpu_seconds)
