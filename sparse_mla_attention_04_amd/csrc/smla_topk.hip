@@ -51,7 +51,14 @@ constexpr int WIDTHS[3] = {11, 11, 10};
 // Candidate keys (and indices) held in LDS: the one-read route's keys >= tau
 // (about 3072 for k = 2048), or the two-read route's top-digit bucket (about
 // 1200 for N(0,1) scores, 65536 keys, k = 2048).
-constexpr int CAP = 4096;
+// 4084 rather than 4096: with it the work-group's LDS (histogram,
+// candidates, counters) is 40,912 bytes, so four work-groups share a CU.
+constexpr int CAP = 4084;
+// The one-read route runs for k <= KMAX_ONE: its threshold aims at
+// (k + CAP) / 2 keys, which leaves (CAP - k) / 2 keys of room below CAP and
+// above k.
+constexpr int KMAX_ONE = 2048;
+static_assert((CAP - KMAX_ONE) / 2 >= 1000, "one-read route margin");
 // One-read route: sampled lines are every LSTRIDE-th 128-byte line, at most
 // CAP sample keys, and the sample rank r behind tau at least MIN_RANK (the
 // count of row keys >= tau then has a relative spread of at most about
@@ -243,7 +250,7 @@ __global__ void __launch_bounds__(256) smla_topk_kernel(TopkArgs a) {
   };
 
   // ---- one read: a sampled threshold, then one pass collecting keys >= tau
-  if (vec && k <= CAP / 2) {
+  if (vec && k <= KMAX_ONE) {
     const int lines = len >> 5;                       // whole 128-byte lines of the row
     const int nsl_all = lines / LSTRIDE;              // sampled lines
     const int nsl = nsl_all < CAP / 32 ? nsl_all : CAP / 32;
