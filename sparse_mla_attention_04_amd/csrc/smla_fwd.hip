@@ -181,6 +181,36 @@ __device__ __forceinline__ void dma16(const void* gaddr, uint32_t m0) {
                : "memory", "m0");
 }
 
+// The KS 16-byte pieces of a lane's query (k-step kk at qp + 32 kk bf16
+// elements) to LDS bytes qd + 1024 kk + 16 lane: one direct-to-LDS load per
+// k-step, each covering 1 KB of contiguous LDS for the wave.
+template <int KS>
+__device__ __forceinline__ void dma_queries(const uint16_t* qp, uint32_t qd) {
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    switch (kk) {   // dma16 writes LDS at m0 + offset + 16 lane
+      case 0: dma16<0>(qp, qd); break;
+      case 1: dma16<64>(qp, qd + 1 * 960); break;
+      case 2: dma16<128>(qp, qd + 2 * 960); break;
+      case 3: dma16<192>(qp, qd + 3 * 960); break;
+      case 4: dma16<256>(qp, qd + 4 * 960); break;
+      case 5: dma16<320>(qp, qd + 5 * 960); break;
+      case 6: dma16<384>(qp, qd + 6 * 960); break;
+      case 7: dma16<448>(qp, qd + 7 * 960); break;
+      case 8: dma16<512>(qp, qd + 8 * 960); break;
+      case 9: dma16<576>(qp, qd + 9 * 960); break;
+      case 10: dma16<640>(qp, qd + 10 * 960); break;
+      case 11: dma16<704>(qp, qd + 11 * 960); break;
+      case 12: dma16<768>(qp, qd + 12 * 960); break;
+      case 13: dma16<832>(qp, qd + 13 * 960); break;
+      case 14: dma16<896>(qp, qd + 14 * 960); break;
+      case 15: dma16<960>(qp, qd + 15 * 960); break;
+      case 16: dma16<1024>(qp, qd + 16 * 960); break;
+      default: dma16<1088>(qp, qd + 17 * 960); break;
+    }
+  }
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
@@ -597,14 +627,14 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
   // ---- queries of this wave's 16 heads, in the MFMA B-operand layout:
   //      lane (g4, n) holds head hg*16+n, dims 32*kk + 8*g4 .. +7
   bf16x8 qb[18 * S::NE];   // RSPLIT: group e's k-step kk at qb[18e + kk]
-  // QDMA (pipelined h = 64 shapes, not dense): the queries (64 heads x 576
-  // dims = two tiles' bytes) are not loaded here.  Loads retire in issue order
-  // on one counter, so the compaction's wait for its block-table words would
+  // QDMA (the pipelined shapes: h = 64 and dense): the queries (64 heads or
+  // slots x 576 dims = two tiles' bytes) are not loaded here.  Loads retire in
+  // issue order on one counter, so the wait for the block-table words would
   // also wait for 73.7 KB of queries requested before them.  They are instead
   // requested once those words have landed, straight into ring slots 2..3
   // (idle until the first tiles are gathered), and read into registers after
   // tiles 0..1 are issued and before slots 2..3 are.
-  constexpr bool QDMA = S::PV32 && !S::DENSE;
+  constexpr bool QDMA = S::PV32;
   if constexpr (QDMA) {
 #pragma unroll
     for (int kk = 0; kk < 18; ++kk) qb[kk] = bf16x8{};
@@ -651,13 +681,27 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
     seq_ok = (seq >= 0 && seq < a.num_seqs);
     bt_row = seq_ok ? (int64_t)seq * a.bt_stride : 0;
   }
-  // dense mode: this slot's causal limit, and the block's largest one
+  // dense mode: this slot's causal limit, and the sequence's block-table row
+  // (max_blocks <= LIST_CAP words, requested with the limits so that one round
+  // trip brings both); then the queries, once both have landed
   int d_plim = 0;
+  int d_btw[S::DENSE ? LIST_CAP / S::NTHR : 1];
   if constexpr (S::DENSE) {
     const int lastpos = a.max_blocks * (1 << a.page_shift) - 1;   // beyond the block table: skipped
     int pl = a.positions[d_r0 + d_row];
+#pragma unroll
+    for (int j = 0; j < LIST_CAP / S::NTHR; ++j) {
+      const int i = tid + j * S::NTHR;
+      d_btw[j] = (i < a.max_blocks) ? a.block_table[bt_row + i] : -1;
+    }
     pl = pl < lastpos ? pl : lastpos;
     d_plim = pl;
+    asm volatile("" : : "v"(pl));
+#pragma unroll
+    for (int j = 0; j < LIST_CAP / S::NTHR; ++j) asm volatile("" : : "v"(d_btw[j]));
+    // slot m = 16 hg + n is (row d_row, head d_head) of the block
+    const uint16_t* qp = a.q + (int64_t)(d_r0 + d_row) * a.q_st + (int64_t)d_head * a.q_sh + 8 * g4;
+    dma_queries<S::KS>(qp, ring0 + 2u * S::TILE_BYTES + (uint32_t)(hg * S::KS) * 1024u);
   }
 
   for (int pass = 0; pass < 2; ++pass) {
@@ -681,9 +725,10 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
       for (int w = 1; w < S::NW; ++w) bm = fmaxf(bm, wmax[w]);
       const int pmax = (int)bm;
       const int npg = (pmax >> a.page_shift) + 1;
-      for (int i = tid; i < npg; i += S::NTHR) {
-        const int pg = a.block_table[bt_row + i];
-        list[i] = (pg >= 0 && pg < a.num_pages) ? pg : -1;
+#pragma unroll
+      for (int j = 0; j < LIST_CAP / S::NTHR; ++j) {
+        const int i = tid + j * S::NTHR;
+        if (i < npg) list[i] = (d_btw[j] >= 0 && d_btw[j] < a.num_pages) ? d_btw[j] : -1;
       }
       __syncthreads();
       n_valid = pmax + 1;
@@ -697,30 +742,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
             // read head 0 and are zeroed when read out)
             const int head = hg * 16 + n;
             const uint16_t* qp = a.q + (int64_t)t * a.q_st + (int64_t)(head < a.h ? head : 0) * a.q_sh + 8 * g4;
-            const uint32_t qd = ring0 + 2u * S::TILE_BYTES + (uint32_t)(hg * S::KS) * 1024u;
-#pragma unroll
-            for (int kk = 0; kk < S::KS; ++kk) {
-              switch (kk) {   // dma16 writes LDS at m0 + offset + 16 lane
-                case 0: dma16<0>(qp, qd); break;
-                case 1: dma16<64>(qp, qd + 1 * 960); break;
-                case 2: dma16<128>(qp, qd + 2 * 960); break;
-                case 3: dma16<192>(qp, qd + 3 * 960); break;
-                case 4: dma16<256>(qp, qd + 4 * 960); break;
-                case 5: dma16<320>(qp, qd + 5 * 960); break;
-                case 6: dma16<384>(qp, qd + 6 * 960); break;
-                case 7: dma16<448>(qp, qd + 7 * 960); break;
-                case 8: dma16<512>(qp, qd + 8 * 960); break;
-                case 9: dma16<576>(qp, qd + 9 * 960); break;
-                case 10: dma16<640>(qp, qd + 10 * 960); break;
-                case 11: dma16<704>(qp, qd + 11 * 960); break;
-                case 12: dma16<768>(qp, qd + 12 * 960); break;
-                case 13: dma16<832>(qp, qd + 13 * 960); break;
-                case 14: dma16<896>(qp, qd + 14 * 960); break;
-                case 15: dma16<960>(qp, qd + 15 * 960); break;
-                case 16: dma16<1024>(qp, qd + 16 * 960); break;
-                default: dma16<1088>(qp, qd + 17 * 960); break;
-              }
-            }
+            dma_queries<S::KS>(qp, ring0 + 2u * S::TILE_BYTES + (uint32_t)(hg * S::KS) * 1024u);
           }
         }
       });
@@ -1340,7 +1362,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
           const LDS_AS uint8_t* qs = lds + 2 * S::TILE_BYTES + hg * S::KS * 1024 + 16 * lane;
 #pragma unroll
           for (int kk = 0; kk < S::KS; ++kk) qb[kk] = *reinterpret_cast<const LDS_AS bf16x8*>(qs + 1024 * kk);
-          if (hg * 16 + n >= a.h) {
+          if (!S::DENSE && hg * 16 + n >= a.h) {
 #pragma unroll
             for (int kk = 0; kk < S::KS; ++kk) qb[kk] = bf16x8{};
           }
