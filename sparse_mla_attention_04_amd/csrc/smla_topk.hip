@@ -267,6 +267,23 @@ __global__ void __launch_bounds__(256) smla_topk_kernel(TopkArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) cand_key[4 * j + q] = order_key(v[q]);
       }
+      // batches of U 16-byte loads per thread, all issued before any key of
+      // the batch is examined (the appends branch, which would otherwise
+      // leave one load in flight per wave), the next batch requested before
+      // the current one is examined; the first batch is requested here, so
+      // that it is in flight while the sample's digits are selected (the
+      // barriers of that selection wait for LDS operations only)
+      const int n4 = len >> 2;
+      constexpr int U = 8;
+      f32x4 cur[U], nxt[U];
+      auto load_batch = [&](int j0, f32x4 (&v)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int j = j0 + u * 256 + tid;
+          v[u] = row4[j < n4 ? j : n4 - 1];
+        }
+      };
+      if (n4 > 0) load_batch(0, cur);
       __syncthreads();
       kr = (int)rank;
       // two of the three digits: tau is the lowest key of the 22-bit bucket
@@ -282,7 +299,6 @@ __global__ void __launch_bounds__(256) smla_topk_kernel(TopkArgs a) {
       __syncthreads();
       if (tid == 0) ctl[3] = 0;
       __syncthreads();
-      const int n4 = len >> 2;
       auto append = [&](uint32_t u, int i, bool ok) {
         if (ok && u >= tau) {
           const int c = atomicAdd(&ctl[3], 1);
@@ -292,20 +308,6 @@ __global__ void __launch_bounds__(256) smla_topk_kernel(TopkArgs a) {
           }
         }
       };
-      // batches of U 16-byte loads per thread, all issued before any key of
-      // the batch is examined (the appends branch, which would otherwise
-      // leave one load in flight per wave), the next batch requested before
-      // the current one is examined
-      constexpr int U = 8;
-      f32x4 cur[U], nxt[U];
-      auto load_batch = [&](int j0, f32x4 (&v)[U]) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int j = j0 + u * 256 + tid;
-          v[u] = row4[j < n4 ? j : n4 - 1];
-        }
-      };
-      if (n4 > 0) load_batch(0, cur);
       for (int j0 = 0; j0 < n4; j0 += 256 * U) {
         if (j0 + 256 * U < n4) load_batch(j0 + 256 * U, nxt);
         uint32_t key[U][4];
