@@ -159,6 +159,18 @@ int make_plan(const smla_params* p, int32_t num_cus, smla_plan* plan) {
 std::mutex g_mu;
 int g_cus[256];
 
+// Keys per indexer work unit: each unit loads its 16 rows' queries (256 KB at
+// 64 heads) once, so longer chunks load them less often; they are doubled
+// from 4096 up to 16384 keys while at least four units per CU remain
+// (4096 rows x 65536 keys on 256 CUs: 3.29 ms at 4096, 3.24 at 8192, 3.22 at
+// 16384 keys per chunk).
+int indexer_chunk_keys(int32_t row_blocks, int32_t n_keys, int32_t cus) {
+  int chunk = 4096;
+  while (chunk < 16384 && (int64_t)row_blocks * ((n_keys + 2 * chunk - 1) / (2 * chunk)) >= 4 * (int64_t)cus)
+    chunk *= 2;
+  return chunk;
+}
+
 int device_cus(int32_t* cus) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return SMLA_ERR_HIP;
@@ -442,7 +454,12 @@ int sparse_mla_indexer_logits(const void* q, int64_t q_stride_t, int64_t q_strid
   if (!q || !k || !w || !logits) return SMLA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(w, 16) || !aligned(logits, 4) || (lens && !aligned(lens, 4)))
     return SMLA_ERR_INVALID_ARG;
-  constexpr int kChunkKeys = 4096;
+  int32_t cus = 0;
+  const int dev_rc = device_cus(&cus);
+  if (dev_rc != SMLA_OK) return dev_rc;
+  const int rpb = smla::indexer_rows_per_block();
+  const int32_t row_blocks = (num_rows + rpb - 1) / rpb;
+  const int chunk_keys = indexer_chunk_keys(row_blocks, n_keys, cus);
   smla::IndexerArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -457,10 +474,9 @@ int sparse_mla_indexer_logits(const void* q, int64_t q_stride_t, int64_t q_strid
   a.T = num_rows;
   a.n_keys = n_keys;
   a.H = num_heads;
-  a.chunk_keys = kChunkKeys;
-  const int rpb = smla::indexer_rows_per_block();
-  a.row_blocks = (num_rows + rpb - 1) / rpb;
-  a.units = (int64_t)a.row_blocks * ((n_keys + kChunkKeys - 1) / kChunkKeys);
+  a.chunk_keys = chunk_keys;
+  a.row_blocks = row_blocks;
+  a.units = (int64_t)a.row_blocks * ((n_keys + chunk_keys - 1) / chunk_keys);
   const int64_t grid = (a.units + 7) / 8 * 8;
   a.grid_per_xcd = (int32_t)(grid / 8);
   if (smla::launch_indexer(a, grid, static_cast<hipStream_t>(stream)) != hipSuccess) return SMLA_ERR_HIP;
