@@ -1809,7 +1809,7 @@ __global__ void __launch_bounds__(S::NTHR, 1) smla_fwd(FwdArgs a) {
 template <int SMAX>
 __global__ void __launch_bounds__(256) smla_lse_combine(CombineArgs a) {
   const int t = blockIdx.x;
-  const int item = blockIdx.y * 256 + threadIdx.x;
+  const int item = blockIdx.y * blockDim.x + threadIdx.x;
   if (item >= a.h * 64) return;
   const int head = item >> 6, c = item & 63;
   const int S_ = a.num_splits;
@@ -2033,11 +2033,14 @@ hipError_t noalloc_scratch(void** ptr) {
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)a.T, (unsigned)((a.h * 64 + 255) / 256));
-  if (a.num_splits <= 4) hipLaunchKernelGGL(smla_lse_combine<4>, grid, dim3(256), 0, stream, a);
-  else if (a.num_splits <= 8) hipLaunchKernelGGL(smla_lse_combine<8>, grid, dim3(256), 0, stream, a);
-  else if (a.num_splits <= 16) hipLaunchKernelGGL(smla_lse_combine<16>, grid, dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL(smla_lse_combine<0>, grid, dim3(256), 0, stream, a);
+  // one 64-thread work-group per (row, head): a decode batch's few rows still
+  // spread over every CU (c2: 256 work-groups of 16 KB of partials each
+  // instead of 64 of 64 KB; the step 23.8 -> 23.4 us)
+  const dim3 grid((unsigned)a.T, (unsigned)a.h);
+  if (a.num_splits <= 4) hipLaunchKernelGGL(smla_lse_combine<4>, grid, dim3(64), 0, stream, a);
+  else if (a.num_splits <= 8) hipLaunchKernelGGL(smla_lse_combine<8>, grid, dim3(64), 0, stream, a);
+  else if (a.num_splits <= 16) hipLaunchKernelGGL(smla_lse_combine<16>, grid, dim3(64), 0, stream, a);
+  else hipLaunchKernelGGL(smla_lse_combine<0>, grid, dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 
